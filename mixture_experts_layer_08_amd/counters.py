@@ -1,0 +1,58 @@
+"""Algorithmic byte and FLOP counts of the MoE-layer forward.
+
+These are the counted work of each step (what the method must move or
+multiply), not what a kernel happens to read.  They follow the traffic and
+compute formulas of the cf-1.com page "Dissecting the MoE communication
+bottleneck": section 2.1 (dispatch bytes = tokens x top_k x hidden x dtype
+bytes, combine the same) and section 2.2 (expert FFN = 2 x 2 x H x h_exp
+FLOP per token-expert pair).
+"""
+
+from __future__ import annotations
+
+
+def dispatch_bytes(tokens: int, top_k: int, hidden: int, dtype_bytes: int) -> int:
+    """Bytes one layer's dispatch moves: B * K * H * dtype (section 2.1)."""
+    return tokens * top_k * hidden * dtype_bytes
+
+
+def combine_bytes(tokens: int, top_k: int, hidden: int, dtype_bytes: int) -> int:
+    """Combine moves the same payload back (section 2.1)."""
+    return tokens * top_k * hidden * dtype_bytes
+
+
+def ffn_flop_per_assignment(hidden: int, h_exp: int) -> int:
+    """2 x 2 x H x h_exp: two matmuls of 2*H*h FLOP each (section 2.2)."""
+    return 4 * hidden * h_exp
+
+
+def comm_compute_ratio(dtype_bytes: int, h_exp: int) -> float:
+    """Bytes per FLOP of one token-expert pair: 2*H*dtype / (4*H*h) (section 2.3)."""
+    return dtype_bytes / (2.0 * h_exp)
+
+
+# -- per-launch algorithmic work of this library's kernels -------------------
+
+def grouped_gemm_flop_per_launch(n_rows: int, H: int, h: int) -> int:
+    """One grouped-GEMM launch (GEMM1 or GEMM2) over n_rows kept rows: 2*n*H*h."""
+    return 2 * n_rows * H * h
+
+
+def permute_bytes(T: int, n_kept: int, H: int, b: int, K: int) -> int:
+    """Dispatch kernel: each token row read once, each kept row written once,
+    plus the int32 routing ids read and row_of written (T*K each) and token_of
+    written (n_kept)."""
+    return T * H * b + n_kept * H * b + 4 * (2 * T * K + n_kept)
+
+
+def combine_kernel_bytes(T: int, n_kept: int, H: int, b: int, K: int, shared: bool) -> int:
+    """Combine kernel: each kept expert-output row read once, each token row
+    written once (plus the shared-expert row read when present), plus row_of
+    and the fp32 weights read (T*K each)."""
+    return n_kept * H * b + T * H * b * (2 if shared else 1) + 8 * T * K
+
+
+def router_bytes(T: int, H: int, E: int, K: int, b: int) -> int:
+    """Router kernel: x read once, router weight read once, fp32 logits and
+    the top-k ids/weights written."""
+    return T * H * b + H * E * b + 4 * T * E + 8 * T * K
