@@ -1,0 +1,200 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) top-k-routed Mixture-of-Experts layer
+ * forward.
+ *
+ * One forward pass is five calls, issued in this order on one HIP stream:
+ *
+ *   moe_route      router GEMM, softmax, top-k, renormalised weights
+ *   moe_aux_loss   E * sum_e f_e * P_e load-balancing loss
+ *   moe_permute    capacity drop in token order, packed expert-major rows,
+ *                  dispatch copy of the token rows
+ *   moe_expert_ffn grouped GEMM1 + GELU(tanh), grouped GEMM2 (and the
+ *                  optional shared expert)
+ *   moe_combine    weighted un-permute back to token order
+ *
+ * The method is the one of three web pages on MoE layers:
+ *   [infra] "MoE module infra notes" (dpshk.com/news/5154311): the router of
+ *           section 3.1, the expert module of 3.3 and the MoELayer listing of
+ *           4.2 (stacked expert weights, capacity, per-expert contractions).
+ *   [comm]  "Dissecting the MoE communication bottleneck" (cf-1.com/news/
+ *           4950847): dispatch / FFN / combine of section 1.1, capacity and
+ *           token drop of 3.1, the aux-loss formula of 3.2, fine-grained plus
+ *           shared experts of 2.3, grouped GEMM of 5.1.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - All tensors are caller-owned, dense, row-major, device memory.  Pointers
+ *   to the bf16/fp32 activation and weight tensors must be 16-byte aligned.
+ *   "bf16 mode" (dtype MOE_BF16): x, w_router, w1, w2, ws1, ws2, xp, hbuf,
+ *   out, hshared, shared_out and y are bfloat16; accumulation is fp32.
+ *   "fp32 mode" (MOE_F32): all of them are float.  Router bias, logits,
+ *   top-k weights and aux are always float; ids, counts and row maps int32.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream), never allocate, never synchronise the host, and keep row counts
+ *   on the device.  Errors from invalid arguments are returned before any
+ *   launch; device faults surface at the caller's next synchronisation.
+ * - `ws` is a caller-provided device workspace of at least
+ *   moe_workspace_size(shape) bytes (256-byte aligned).  moe_route fills it
+ *   with per-block partial results that moe_aux_loss and moe_permute read, so
+ *   one forward must use one workspace, and calls that share a workspace must
+ *   not overlap.
+ * - Results are deterministic: no floating-point atomics, fixed reduction
+ *   orders.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer  */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels support  */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes below moe_workspace_size()         */
+  MOE_ERR_HIP = 4            /* a HIP launch or runtime call failed          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* moe_shape.flags */
+#define MOE_FLAG_LOGITS_IN 1u  /* moe_route reads `logits` instead of running the router GEMM */
+
+typedef struct {
+  int32_t T;        /* tokens in the batch                                   */
+  int32_t H;        /* hidden size (multiple of 8)                           */
+  int32_t E;        /* routed experts, 1..256                                */
+  int32_t K;        /* experts per token (top-k), 1..min(E, 8)               */
+  int32_t h_exp;    /* expert FFN width (multiple of 8)                      */
+  int32_t h_shared; /* shared-expert FFN width (multiple of 8), 0 = none     */
+  float capacity_factor; /* > 0: C = ceil(cf*T*K/E); <= 0: no limit (C = T)  */
+  int32_t dtype;    /* moe_dtype                                             */
+  uint32_t flags;   /* MOE_FLAG_*                                            */
+} moe_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Validates `s` alone (sizes, dtype, flags); MOE_OK when the shape is usable. */
+moe_status moe_check_shape(const moe_shape* s);
+
+/* Expert capacity C: ceil(cf*T*K/E) computed in double for cf > 0, else T
+ * ([comm] 3.1, read with T*K assignments), capped at T since no expert can
+ * receive more than T assignments (the cap never changes which rows are
+ * kept).  -1 for an invalid shape. */
+int64_t moe_capacity(const moe_shape* s);
+
+/* Upper bound on kept rows N = sum_e min(count_e, C): min(T*K, E*C).  xp and
+ * out need this many rows, hbuf this many rows of h_exp.  -1 if invalid. */
+int64_t moe_max_rows(const moe_shape* s);
+
+/* Bytes of device workspace every call of one forward needs (0 if invalid). */
+size_t moe_workspace_size(const moe_shape* s);
+
+/*
+ * moe_route - router logits, softmax, top-k and renormalised weights
+ * ([infra] 3.1 and 4.2; [comm] 1.1 step 1; inference top-k on logits,
+ * [infra] 5.2 tip 4).
+ *
+ *   x        [T,H]   token rows (dtype)
+ *   w_router [H,E]   router weight (dtype)
+ *   b_router [E]     fp32 router bias, or NULL for none
+ *   logits   [T,E]   fp32 out: x*W_r + b accumulated in fp32.  With
+ *                    MOE_FLAG_LOGITS_IN it is an input and x / w_router /
+ *                    b_router are ignored (may be NULL).
+ *   topk_ids [T,K]   int32 out: the K experts with the largest logits, slot 0
+ *                    the largest; equal logits go to the lower expert index.
+ *   topk_w   [T,K]   fp32 out: p[t,e]/sum_{chosen} p[t,e'] with p the softmax
+ *                    of the logits row (no noise, temperature 1).
+ *   ws               workspace; receives per-block expert histograms, in-block
+ *                    ranks and per-block softmax column sums.
+ * Logits must be finite (not checked).
+ */
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_router,
+                     const float* b_router, float* logits, int32_t* topk_ids,
+                     float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_aux_loss - aux = E * sum_e f_e * P_e ([comm] 3.2), f_e = count_e/(T*K)
+ * from the pre-drop top-k choices, P_e = mean over all T tokens of the full
+ * softmax probability of e.  No coefficient is applied.  Reads the workspace
+ * filled by the preceding moe_route.
+ *
+ *   aux      [1]     fp32 out (device)
+ */
+moe_status moe_aux_loss(const moe_shape* s, const void* ws, size_t ws_bytes,
+                        float* aux, void* stream);
+
+/*
+ * moe_permute - capacity drop, packed row map and dispatch copy
+ * ([comm] 1.1 step 2 and 3.1; [infra] 4.2 expert counts and capacity).
+ *
+ * Assignment (t,k) to e = topk_ids[t,k] has rank r = #{t' < t : e chosen by
+ * t'}; it is kept iff r < C.  Kept rows of expert e form the contiguous
+ * segment [offsets[e], offsets[e+1]) in token order.
+ *
+ *   x         [T,H]      token rows (dtype)
+ *   topk_ids  [T,K]      from moe_route (same workspace)
+ *   counts    [E]        int32 out: pre-drop assignments per expert
+ *   kept      [E]        int32 out: min(counts, C)
+ *   offsets   [E+1]      int32 out: exclusive prefix sum of kept; N = offsets[E]
+ *   row_of    [T,K]      int32 out: packed row of (t,k), -1 when dropped
+ *   token_of  [max_rows] int32 out: token of each packed row (rows >= N untouched)
+ *   n_dropped [1]        int32 out: sum_e (counts - kept)
+ *   xp        [max_rows,H] out (dtype): xp[row_of[t,k]] = x[t]; rows >= N untouched
+ */
+moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_ids,
+                       void* ws, size_t ws_bytes, int32_t* counts, int32_t* kept,
+                       int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                       int32_t* n_dropped, void* xp, void* stream);
+
+/*
+ * moe_expert_ffn - grouped expert FFN over the packed segments
+ * ([infra] 3.3 and the per-expert contractions of 4.2; [comm] 2.2 FLOP count,
+ * 5.1 grouped GEMM; shared expert [comm] 2.3).
+ *
+ *   hbuf[r] = GELU_tanh(xp[r] * W1[e])   (fp32 accumulate, GELU in fp32,
+ *                                         stored in dtype)
+ *   out[r]  = hbuf[r] * W2[e]            (fp32 accumulate, stored in dtype)
+ * for every row r of segment e.  With h_shared > 0 also
+ *   hshared = GELU_tanh(x * Ws1), shared_out = hshared * Ws2 over all T rows.
+ *
+ *   xp       [max_rows,H]     packed rows from moe_permute
+ *   offsets  [E+1]            int32 device segment bounds from moe_permute
+ *   w1       [E,H,h_exp], w2 [E,h_exp,H]   expert weights (dtype)
+ *   hbuf     [max_rows,h_exp] scratch out (dtype)
+ *   out      [max_rows,H]     out (dtype); rows >= N untouched
+ *   x, ws1 [H,h_shared], ws2 [h_shared,H], hshared [T,h_shared],
+ *   shared_out [T,H]          used only when h_shared > 0 (else may be NULL)
+ */
+moe_status moe_expert_ffn(const moe_shape* s, const void* xp, const int32_t* offsets,
+                          const void* w1, const void* w2, void* hbuf, void* out,
+                          const void* x, const void* ws1, const void* ws2,
+                          void* hshared, void* shared_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine - y[t] = sum_{k : row_of[t,k] >= 0} topk_w[t,k] * out[row_of[t,k]]
+ * (+ shared_out[t]), accumulated in fp32 in slot order, then rounded to dtype
+ * ([comm] 1.1 step 4).  Dropped slots contribute zero and the kept weights
+ * are not renormalised; a token with every slot dropped gets 0 (plus its
+ * shared-expert row).
+ *
+ *   out        [max_rows,H] expert outputs (dtype)
+ *   row_of     [T,K], topk_w [T,K]
+ *   shared_out [T,H] or NULL
+ *   y          [T,H] out (dtype)
+ */
+moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_of,
+                       const float* topk_w, const void* shared_out, void* y,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

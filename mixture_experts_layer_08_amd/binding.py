@@ -1,0 +1,168 @@
+"""ctypes binding of libmoe.so (include/moe.h), one function per C entry point.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+a hipStream_t handle, and a non-OK status raises :class:`MoeError`.  All
+computation happens in the library's HIP kernels.  The library must have been
+built (``python -m mixture_experts_layer_08_amd.build``); loading fails loudly
+otherwise, there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_FLAG_LOGITS_IN = 1
+
+# Every symbol include/moe.h declares.
+EXPORTS = (
+    "moe_status_string", "moe_check_shape", "moe_capacity", "moe_max_rows",
+    "moe_workspace_size", "moe_route", "moe_aux_loss", "moe_permute",
+    "moe_expert_ffn", "moe_combine",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("K", ctypes.c_int32), ("h_exp", ctypes.c_int32), ("h_shared", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_shape(T, H, E, K, h_exp, h_shared=0, capacity_factor=0.0, dtype=MOE_BF16, flags=0):
+    return moe_shape(T, H, E, K, h_exp, h_shared, capacity_factor, dtype, flags)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_SHAPE = ctypes.POINTER(moe_shape)
+
+
+def lib():
+    """Load libmoe.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_08_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_check_shape.restype = ctypes.c_int
+        L.moe_check_shape.argtypes = [_SHAPE]
+        L.moe_capacity.restype = ctypes.c_int64
+        L.moe_capacity.argtypes = [_SHAPE]
+        L.moe_max_rows.restype = ctypes.c_int64
+        L.moe_max_rows.argtypes = [_SHAPE]
+        L.moe_workspace_size.restype = _SZ
+        L.moe_workspace_size.argtypes = [_SHAPE]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_aux_loss.restype = ctypes.c_int
+        L.moe_aux_loss.argtypes = [_SHAPE, _P, _SZ, _P, _P]
+        L.moe_permute.restype = ctypes.c_int
+        L.moe_permute.argtypes = [_SHAPE, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_expert_ffn.restype = ctypes.c_int
+        L.moe_expert_ffn.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib().moe_status_string(status).decode())
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_check_shape(s: moe_shape) -> int:
+    return lib().moe_check_shape(ctypes.byref(s))
+
+
+def moe_capacity(s: moe_shape) -> int:
+    return lib().moe_capacity(ctypes.byref(s))
+
+
+def moe_max_rows(s: moe_shape) -> int:
+    return lib().moe_max_rows(ctypes.byref(s))
+
+
+def moe_workspace_size(s: moe_shape) -> int:
+    return lib().moe_workspace_size(ctypes.byref(s))
+
+
+def moe_route(s, x, w_router, b_router, logits, topk_ids, topk_w, ws, stream=None):
+    _check("moe_route", lib().moe_route(
+        ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_aux_loss(s, ws, aux, stream=None):
+    _check("moe_aux_loss", lib().moe_aux_loss(
+        ctypes.byref(s), _ptr(ws), _nbytes(ws), _ptr(aux), _stream(stream)))
+
+
+def moe_permute(s, x, topk_ids, ws, counts, kept, offsets, row_of, token_of, n_dropped, xp,
+                stream=None):
+    _check("moe_permute", lib().moe_permute(
+        ctypes.byref(s), _ptr(x), _ptr(topk_ids), _ptr(ws), _nbytes(ws), _ptr(counts),
+        _ptr(kept), _ptr(offsets), _ptr(row_of), _ptr(token_of), _ptr(n_dropped), _ptr(xp),
+        _stream(stream)))
+
+
+def moe_expert_ffn(s, xp, offsets, w1, w2, hbuf, out, x, ws1, ws2, hshared, shared_out, ws,
+                   stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        ctypes.byref(s), _ptr(xp), _ptr(offsets), _ptr(w1), _ptr(w2), _ptr(hbuf), _ptr(out),
+        _ptr(x), _ptr(ws1), _ptr(ws2), _ptr(hshared), _ptr(shared_out), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_combine(s, out, row_of, topk_w, shared_out, y, stream=None):
+    _check("moe_combine", lib().moe_combine(
+        ctypes.byref(s), _ptr(out), _ptr(row_of), _ptr(topk_w), _ptr(shared_out), _ptr(y),
+        _stream(stream)))

@@ -1,0 +1,64 @@
+// Shared device helpers of the gfx950 MoE kernels: vector types, bf16
+// conversion, wave-level scans.  Wavefronts are 64 lanes wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return static_cast<bf16>(f); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = f32_to_bf16(lo), b = f32_to_bf16(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// GELU, tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3).
+// Since 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2z)), this is u / (1 + exp(-2z)),
+// evaluated with the hardware base-2 exponential: exp(-2z) = 2^(-2z log2 e).
+// For u -> -inf the exponential overflows to +inf and the quotient is -0,
+// the limit; for u -> +inf it is u.
+__device__ __forceinline__ float gelu_tanh_f32(float u) {
+  const float kC = 0.7978845608028654f;           // sqrt(2/pi)
+  const float kNeg2Log2e = -2.8853900817779268f;   // -2 / ln 2
+  float z = kC * fmaf(0.044715f * u, u * u, u);
+  float e = __builtin_amdgcn_exp2f(kNeg2Log2e * z);
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace moe
