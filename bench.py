@@ -1,0 +1,202 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+A step is one whole forward (moe_route -> moe_aux_loss -> moe_permute ->
+moe_expert_ffn -> moe_combine) over one batch of seeded synthetic tokens,
+with inputs, weights and buffers resident in HBM before the timed region.
+Default workload: T=32768 tokens (seq 4096 x micro-batch 8), H=4096, E=8,
+top-2, h_exp=14336, bf16, capacity factor 1.25 (the worked example of the
+cf-1.com page "Dissecting the MoE communication bottleneck", section 2.2).
+
+Prints one JSON line: tokens/s of the whole forward, the roofline of the
+dominant kernel (the grouped GEMM, timed with HIP events on its launch stream
+over the timed region), permute / combine / router bandwidth, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s on 1 GPU + grouped-GEMM MFMA% and permute HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector / MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    p = os.path.join(ROOT, "mixture_experts_layer_08_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per grouped-GEMM launch from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, p, n_tokens: int):
+    """The oracle, as it stands, on the first n_tokens tokens of the workload."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    from oracle import moe_oracle as O
+
+    n = min(n_tokens, w.T)
+    f = lambda t: None if t is None else t.detach().cpu().to(torch.float32).numpy()
+    x = f(p["x"][:n])
+    wr, br = f(p["w_r"]), f(p["b_r"])
+    w1, w2, ws1, ws2 = f(p["w1"]), f(p["w2"]), f(p["ws1"]), f(p["ws2"])
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    O.forward(x, wr, br, w1, w2, ws1, ws2, K=w.K, cf=w.cf)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"first {n} of {w.T} tokens of the same workload through the whole float64 "
+                   f"numpy oracle forward (router, routing with capacity on the sub-batch, "
+                   f"expert FFN, combine) in {dt:.1f} s; BLAS threads {threads}, "
+                   f"host cpu_count {os.cpu_count()}"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this build "
+              f"(the layer forward runs on a single GPU's token batch).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_layer_08_amd import binding as B
+    from mixture_experts_layer_08_amd import counters, layer
+    from mixture_experts_layer_08_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[a.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = make_inputs(w, seed=a.seed, device=dev)
+    buf = layer.MoeBuffers.allocate(w, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(a.warmup):
+        layer.forward(buf, p, stream)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(6)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        m = marks[s]
+        m[0].record(stream)
+        layer.route(buf, p, stream)
+        m[1].record(stream)
+        layer.aux_loss(buf, stream)
+        m[2].record(stream)
+        layer.permute(buf, p, stream)
+        m[3].record(stream)
+        layer.expert_ffn(buf, p, stream)
+        m[4].record(stream)
+        layer.combine(buf, stream)
+        m[5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def stage_ms(i):
+        return sum(marks[s][i].elapsed_time(marks[s][i + 1]) for s in range(a.steps)) / a.steps
+
+    route_ms, aux_ms, perm_ms, ffn_ms, comb_ms = (stage_ms(i) for i in range(5))
+    ms_step = wall * 1e3 / a.steps
+    N = int(buf.offsets[-1].item())
+    dropped = int(buf.n_dropped.item())
+    b = 2 if w.dtype == "bf16" else 4
+
+    # dominant kernel: the grouped GEMM, launched twice per step (GEMM1 with
+    # GELU, GEMM2) plus twice more for the shared expert when present
+    launches = 2 + (2 if w.hs else 0)
+    gemm_flop_step = 2 * counters.grouped_gemm_flop_per_launch(N, w.H, w.h)
+    if w.hs:
+        gemm_flop_step += 2 * counters.grouped_gemm_flop_per_launch(w.T, w.H, w.hs)
+    flop_per_launch = gemm_flop_step / launches
+    launch_s = ffn_ms * 1e-3 / launches
+    achieved = flop_per_launch / launch_s / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = traffic_from_profile(w.name)
+
+    perm_bytes = counters.permute_bytes(w.T, N, w.H, b, w.K)
+    comb_bytes = counters.combine_kernel_bytes(w.T, N, w.H, b, w.K, bool(w.hs))
+    route_bytes = counters.router_bytes(w.T, w.H, w.E, w.K, b)
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": w.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, drawn on the GPU)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "top_k": w.K,
+                   "h_exp": w.h, "h_shared": w.hs, "capacity_factor": w.cf,
+                   "kept_rows": N, "dropped_assignments": dropped,
+                   "aux_loss": float(buf.aux.item())},
+        "roofline": {"kernel": "k_grouped_gemm_bf16" if w.dtype == "bf16" else "k_grouped_gemm_f32",
+                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "flop_per_launch": flop_per_launch, "avg_launch_ms": launch_s * 1e3},
+        "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute": perm_ms,
+                      "expert_ffn": ffn_ms, "combine": comb_ms},
+        "hbm": {
+            "permute": {"GB/s": gbs(perm_bytes, perm_ms), "frac": gbs(perm_bytes, perm_ms) / PEAK_HBM_GBS,
+                        "bytes": perm_bytes, "note": "moe_permute: scan, offsets and copy kernels"},
+            "combine": {"GB/s": gbs(comb_bytes, comb_ms), "frac": gbs(comb_bytes, comb_ms) / PEAK_HBM_GBS,
+                        "bytes": comb_bytes},
+            "route": {"GB/s": gbs(route_bytes, route_ms), "frac": gbs(route_bytes, route_ms) / PEAK_HBM_GBS,
+                      "bytes": route_bytes},
+        },
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, p, a.cpu_sample_tokens)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
