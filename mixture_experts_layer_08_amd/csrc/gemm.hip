@@ -8,24 +8,15 @@
 // cf-1.com page "Dissecting the MoE communication bottleneck" recommends
 // (many thin per-expert GEMMs in one kernel).
 //
-// bf16 kernel (gfx950 MFMA):
-//   - workgroup tile BM x BN x BK = 128 x 128 x 64, 256 threads = 4 waves in
-//     a 2 x 2 grid, each wave a 64 x 64 tile of 2 x 2 v_mfma_f32_32x32x16_bf16;
-//   - A (rows x K, K contiguous) is copied to LDS as [row][k];
-//   - B (K x N, N contiguous, the ABI weight layout) is read in 8(k) x 4(n)
-//     blocks, transposed in registers with v_perm_b32 and stored to LDS as
-//     [n][k], so both MFMA operands are one 16-byte LDS read per lane;
-//   - both LDS tiles swizzle their 16-byte chunks (chunk ^ (row & 7)) so a
-//     wave's 32 row reads spread over all banks;
-//   - two LDS buffers: the global loads of step k+1 are in flight while the
-//     MFMAs of step k run, one barrier per step;
-//   - epilogue: optional GELU(tanh) in fp32, round to bf16, staged through
-//     LDS and written as 16-byte row vectors.
-//   - tile order: blocks of 8 M-tiles sweep the N-tiles column by column so
-//     concurrently running workgroups share A rows and B columns in L2.
-//   - the segment of an M-tile is found on the device from offsets with a
-//     wave-wide prefix sum of per-segment tile counts; the grid is sized for
-//     the worst case and surplus workgroups exit at once (no host sync).
+// The bf16 kernel's design is described above k_grouped_gemm_bf16 below:
+// 256 x 256 x 32 tiles on four waves, a 4-stage LDS ring filled by direct
+// HBM->LDS loads, the N-contiguous weight operand read through LDS transpose
+// reads, and an epilogue with the optional GELU(tanh) straight from the
+// accumulators.  Segment lookup happens on the device from `offsets` (a
+// wave-wide prefix sum of per-segment tile counts); the grid is sized for the
+// worst case and surplus workgroups exit at once, so there is no host sync.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,8 +24,13 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kGroupM = 8;
+#ifndef MOE_GEMM_GROUP_M
+#define MOE_GEMM_GROUP_M 8
+#endif
+#ifndef MOE_GEMM_XCD_REMAP
+#define MOE_GEMM_XCD_REMAP 0
+#endif
+constexpr int kGroupM = MOE_GEMM_GROUP_M;
 
 // Finds the segment of global M-tile `mt`.  Wave-uniform result (every wave
 // of the workgroup computes the same), so an early exit is workgroup-uniform.
@@ -89,140 +85,231 @@ __device__ __forceinline__ void decode_tile(int tile, int mt_bound, int nt_count
   nt = in_g / gsize;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)) << 3; }
-
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void k_grouped_gemm_bf16(
+// XCD-aware order: the hardware hands workgroup i to XCD i % 8.  Remap so
+// that each XCD walks a contiguous range of logical tiles, which the group-M
+// order turns into a compact block of (M-tile, N-tile) pairs sharing A rows
+// and B columns in that XCD's L2.  Returns -1 for padding workgroups.
+__device__ __forceinline__ int xcd_remap(int i, int n_logical) {
+  constexpr int kXcd = 8;
+  if (!MOE_GEMM_XCD_REMAP) return i < n_logical ? i : -1;
+  const int per = (n_logical + kXcd - 1) / kXcd;
+  const int l = (i % kXcd) * per + i / kXcd;
+  return l < n_logical ? l : -1;
+}
+
+
+constexpr uint32_t kOob = 0x80000000u;  // an offset past any num_records
+
+// 256 x 256 tile, BK = 32, 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4
+// MFMA 32x32x16 tiles (256 fp32 accumulators per lane, in AGPRs).
+//
+// Both operands go from HBM/L2 straight into LDS (buffer_load_dwordx4 ...
+// lds, no register staging) through a ring of kStages stages, each K-step's
+// loads issued kStages-1 steps before it is consumed, so that an L2 miss is
+// hidden behind several steps of MFMA work.  One s_barrier per K-step; the
+// wait for a stage's loads is an explicit vmcnt.
+//
+// LDS stage (32 KiB): A [256 m][32 k] (64-byte rows, 16-byte chunk c stored
+// at c ^ ((m >> 2) & 3)) then B [32 k][256 n] (512-byte rows, 16-byte chunk c
+// stored at c ^ (4 * (k & 3))).  Each LDS-direct instruction of a wave fills
+// 1 KiB in lane order; a lane fetches the global chunk that the swizzle maps
+// to its slot.
+//
+// The MFMA runs with the operands swapped (B^T fragment as "A"), so each lane
+// accumulates C^T: per 32x32 tile it owns row m = lane%32 and columns
+// 8*(r/4) + 4*(lane/32) + r%4.  The B^T fragment (8 consecutive k of one n per
+// lane) comes from two ds_read_b64_tr_b16 on the row-major B stage: within
+// each 16-lane group, lane i supplies the address of 4 consecutive n of row
+// (i / 4) and receives column i of that 4 x 16 block.
+constexpr int BM2 = 256, BN2 = 256, BK2 = 32;
+constexpr int kStages = 4;
+constexpr uint32_t kStageBytes = (BM2 + BN2) * BK2 * 2;     // 32 KiB
+constexpr size_t kSmem2 = (size_t)kStages * kStageBytes;    // 128 KiB
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  return *(const lds_bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(uint32_t addr, uint32_t addr_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr_hi);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Raw buffer descriptor (dwords: base lo, base hi, num_records, format) for
+// the inline-asm LDS-DMA load below; base and size must be wave-uniform.
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, long long bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t n = bytes > 0x7ffffff0LL ? 0x7ffffff0u : (bytes < 0 ? 0u : (uint32_t)bytes);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, 0x00020000u};
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_addr + 16 * lane (wave-uniform lds_addr).  Issued as inline asm so the
+// compiler does not treat it as an LDS store that every later LDS read must
+// wait for: the ring's explicit vmcnt waits and barriers order it instead.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C,
-    const int32_t* __restrict__ offsets, int G, int fixed_rows, int mt_bound, int Kd, int N,
-    int gelu) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM * BK + BN * BK)];
-  const int nt_count = (N + BN - 1) / BN;
+    const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows, int mt_bound,
+    int Kd, int N, int gelu) {
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  const int nt_count = (N + BN2 - 1) / BN2;
+  const int logical = xcd_remap(blockIdx.x, mt_bound * nt_count);
+  if (logical < 0) return;
   int mt, nt;
-  decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
+  decode_tile(logical, mt_bound, nt_count, mt, nt);
   int seg, row0, rows;
-  if (!find_segment<BM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  // The lookup result is wave-uniform; keep it in scalar registers so the
+  // buffer descriptors below are scalar too.
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int rr = lane & 31, kh = lane >> 5;
-  const int n0 = nt * BN;
-  const bf16* Bg = B + (size_t)seg * Kd * N;
+  const int n0 = nt * BN2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // A loader: 4 vectors of 8 bf16 per thread: row a_r[j], k-chunk a_c.
-  const int a_c = tid & 7;
-  int a_r[4];
-  bool a_ok[4];
-  const bf16* a_src[4];
+  // ---- global -> LDS loaders (4 + 4 instructions per wave per stage) ----
+  // A: rows [row0, a_rows) of the buffer are addressable; rows past the
+  // segment are read but their outputs never stored.
+  const u32x4 ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
+  // instruction q of this wave covers rows 16*(4q + wave) .. +15
+  const int a_row_l = lane >> 2;                                    // + 16 * (4q + wave)
+  const int a_chunk = (lane & 3) ^ ((a_row_l >> 2) & 3);            // logical chunk of slot
+  const uint32_t a_off = (uint32_t)((a_row_l + 16 * wave) * Kd + a_chunk * 8) * 2;
+  const uint32_t a_qstride = (uint32_t)(64 * Kd) * 2;
+  // B: this expert's slice from column n0 on; k rows past Kd are out of range.
+  const u32x4 rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
+  // instruction q of this wave covers k rows 2*(4q + wave) .. +1
+  const int b_row_l = lane >> 5;                                    // + 2 * (4q + wave)
+  const int b_row0 = b_row_l + 2 * wave;                            // (row & 3) is q-invariant
+  const int b_chunk = (lane & 31) ^ (4 * (b_row0 & 3));
+  const uint32_t b_off = (uint32_t)(b_row0 * N + b_chunk * 8) * 2;
+  const uint32_t b_qstride = (uint32_t)(8 * N) * 2;
+
+  auto issue = [&](int kt) {
+    const int k0 = kt * BK2;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt % kStages) * kStageBytes);
+    const bool kok = k0 + a_chunk * 8 < Kd;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dma_load16(st + (4 * q + wave) * 1024, kok ? a_off + q * a_qstride + (uint32_t)k0 * 2 : kOob,
+                 ra_src);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dma_load16(st + BM2 * BK2 * 2 + (4 * q + wave) * 1024,
+                 b_off + q * b_qstride + (uint32_t)k0 * N * 2, rb_src);
+  };
+
+  // ---- LDS -> register operand addresses (relative to a stage) ----
+  // A fragment i, substep ks: row wm*128 + i*32 + rr, chunk 2ks + kh.
+  uint32_t a_rd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    a_rd[ks] = (uint32_t)(wm * 128 + rr) * 64 + (uint32_t)(((2 * ks + kh) ^ ((rr >> 2) & 3)) * 16);
+  // B^T fragment j: lane group g = lane/16, i = lane%16 reads k row
+  // (g>>1)*8 + i/4 (+4 for the high half, +16 per substep) at n =
+  // wn*128 + j*32 + (g&1)*16 + 4*(i%4).
+  const int bg = lane >> 4, bi = lane & 15;
+  const int b_krow = (bg >> 1) * 8 + (bi >> 2);
+  uint32_t b_rd[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    a_r[j] = (tid >> 3) + 32 * j;
-    a_ok[j] = a_r[j] < rows;
-    a_src[j] = A + (size_t)(row0 + (a_ok[j] ? a_r[j] : 0)) * Kd + a_c * 8;
+    const int n = wn * 128 + j * 32 + (bg & 1) * 16 + 4 * (bi & 3);
+    const int chunk = (n >> 3) ^ (4 * (b_krow & 3));
+    b_rd[j] = BM2 * BK2 * 2 + (uint32_t)b_krow * 512 + (uint32_t)chunk * 16 + (uint32_t)(n & 7) * 2;
   }
-  // B loader: an 8(k) x 4(n) block per thread.
-  const int b_kb = tid >> 5, b_nb = tid & 31;
-  const int b_n = n0 + b_nb * 4;
-  const bool b_nok = b_n < N;
-  const bf16* b_src = Bg + (size_t)(b_kb * 8) * N + (b_nok ? b_n : 0);
 
-  u32x4 ra[4];
-  u32x2 rb[8];
-  auto gload = [&](int k0) {
+  f32x16 acc[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = a_ok[j] && (k0 + a_c * 8 < Kd);
-      ra[j] = ok ? *(const u32x4*)(a_src[j] + k0) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = b_nok && (k0 + b_kb * 8 + i < Kd);
-      rb[i] = ok ? *(const u32x2*)(b_src + (size_t)(k0 + i) * N) : u32x2{0, 0};
-    }
-  };
-  auto lstore = [&](int buf) {
-    bf16* sA = smem + buf * (BM * BK + BN * BK);
-    bf16* sB = sA + BM * BK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4*)(sA + a_r[j] * BK + swz(a_r[j], a_c)) = ra[j];
-#pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const uint32_t sel = (jn & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 o;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        o[m] = __builtin_amdgcn_perm(rb[2 * m + 1][jn >> 1], rb[2 * m][jn >> 1], sel);
-      const int n = b_nb * 4 + jn;
-      *(u32x4*)(sB + n * BK + swz(n, b_kb)) = o;
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = (Kd + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const bf16* sA = smem + buf * (BM * BK + BN * BK);
-    const bf16* sB = sA + BM * BK;
+  const int KT = (Kd + BK2 - 1) / BK2;
+  // prologue: stages 0 .. kStages-2 in flight
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = ks * 2 + kh;
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + rr;
-        a[i] = *(const bf16x8*)(sA + r * BK + swz(r, chunk));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wn * 64 + j * 32 + rr;
-        b[j] = *(const bf16x8*)(sB + n * BK + swz(n, chunk));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  for (int s = 0; s < kStages - 1; ++s) issue(s);
 
-  // Epilogue through LDS: D layout of a 32x32 tile: lane holds column lane%32,
-  // rows 8*(r/4) + 4*(lane/32) + r%4 for its 16 registers r.
-  constexpr int CS = BN + 8;
-  bf16* sC = smem;
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads of step kt are done once at most (kStages-2) later
+    // stages' 8 instructions each are still outstanding
+    wait_vmcnt<(kStages - 2) * 8>();
+    block_barrier();  // every wave's step-kt data in LDS; step kt-1 fully consumed
+    issue(kt + kStages - 1);  // refills the slot of step kt-1 (past K: zeros)
+    const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[4], b[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i) a[i] = lds_read_b128(st + a_rd[ks] + i * 2048);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const int col = wn * 64 + j * 32 + rr;
-        float v = acc[i][j][r];
-        if (gelu) v = gelu_tanh_f32(v);
-        sC[row * CS + col] = f32_to_bf16(v);
+      for (int j = 0; j < 4; ++j)
+        b[j] = lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
+
+  // Epilogue straight from registers: lane owns row m of each 32x32 tile and
+  // four runs of 4 consecutive columns.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + i * 32 + rr;
+    if (m >= rows) continue;
+    bf16* crow = C + (size_t)(row0 + m) * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * kh;
+        if (n < N) {
+          float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+          float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+          if (gelu) {
+            v0 = gelu_tanh_f32(v0);
+            v1 = gelu_tanh_f32(v1);
+            v2 = gelu_tanh_f32(v2);
+            v3 = gelu_tanh_f32(v3);
+          }
+          *(u32x2*)(crow + n) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
       }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < (BM * BN / 8) / 256; ++q) {
-    const int v = tid + 256 * q;
-    const int r = v / (BN / 8), c = v % (BN / 8);
-    if (r < rows && n0 + c * 8 < N)
-      *(u32x4*)(C + (size_t)(row0 + r) * N + n0 + c * 8) = *(const u32x4*)(sC + r * CS + c * 8);
+    }
   }
 }
 
@@ -288,14 +375,23 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
 }
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st) {
-  const int mtb = mt_bound_for(a, BM);
-  const int ntc = (a.N + BN - 1) / BN;
-  const long long grid = (long long)mtb * ntc;
-  if (grid <= 0) return hipSuccess;
+  static bool lds_ok = false;
+  if (!lds_ok) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_bf16,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kSmem2);
+    if (e != hipSuccess) return e;
+    lds_ok = true;
+  }
+  const int mtb = mt_bound_for(a, BM2);
+  const int ntc = (a.N + BN2 - 1) / BN2;
+  const long long n_logical = (long long)mtb * ntc;
+  if (n_logical <= 0) return hipSuccess;
+  const long long grid = (n_logical + 7) / 8 * 8;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_grouped_gemm_bf16<<<(unsigned)grid, 256, 0, st>>>((const bf16*)a.A, (const bf16*)a.B,
-                                                      (bf16*)a.C, a.offsets, a.G, a.fixed_rows,
-                                                      mtb, a.Kd, a.N, a.gelu);
+  k_grouped_gemm_bf16<<<(unsigned)grid, 256, kSmem2, st>>>(
+      (const bf16*)a.A, (const bf16*)a.B, (bf16*)a.C, a.offsets, a.G, a.fixed_rows,
+      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.Kd, a.N, a.gelu);
   return hipGetLastError();
 }
 
