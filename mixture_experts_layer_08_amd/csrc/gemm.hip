@@ -25,12 +25,26 @@ namespace moe {
 namespace {
 
 #ifndef MOE_GEMM_GROUP_M
-#define MOE_GEMM_GROUP_M 8
+#define MOE_GEMM_GROUP_M 4
 #endif
 #ifndef MOE_GEMM_XCD_REMAP
 #define MOE_GEMM_XCD_REMAP 0
 #endif
+// Tile order of the bf16 kernel: 0 = group-M sweep (decode_tile), 1 = XCD
+// panels (decode_tile_xcd).
+#ifndef MOE_GEMM_ORDER
+#define MOE_GEMM_ORDER 0
+#endif
+#ifndef MOE_GEMM_MT_PER_XCD
+#define MOE_GEMM_MT_PER_XCD 4
+#endif
+#ifndef MOE_GEMM_NT_PER_BLOCK
+#define MOE_GEMM_NT_PER_BLOCK 8
+#endif
 constexpr int kGroupM = MOE_GEMM_GROUP_M;
+constexpr int kXcds = 8;
+constexpr int kMtPerXcd = MOE_GEMM_MT_PER_XCD;
+constexpr int kNtPerBlock = MOE_GEMM_NT_PER_BLOCK;
 
 // Finds the segment of global M-tile `mt`.  Wave-uniform result (every wave
 // of the workgroup computes the same), so an early exit is workgroup-uniform.
@@ -85,6 +99,32 @@ __device__ __forceinline__ void decode_tile(int tile, int mt_bound, int nt_count
   nt = in_g / gsize;
 }
 
+// XCD panels.  The hardware hands workgroup i to XCD i % 8.  Workgroups are
+// taken in blocks of 8 * kMtPerXcd * kNtPerBlock: block b covers M-tiles
+// [P*8*kMtPerXcd, +8*kMtPerXcd) of panel P and N-tiles [c*kNtPerBlock,
+// +kNtPerBlock) of chunk c (panel-major), and inside a block XCD x owns M-tiles
+// x*kMtPerXcd .. +kMtPerXcd-1 against all the block's N-tiles.  So each XCD's
+// L2 holds a few A row blocks and the block's B column blocks, and every XCD
+// reads the same B blocks at the same time (shared through the Infinity
+// Cache).  Returns false for slots outside the tile grid.
+__device__ __forceinline__ bool decode_tile_xcd(int i, int mt_bound, int nt_count, int& mt,
+                                                int& nt) {
+  constexpr int kBlock = kXcds * kMtPerXcd * kNtPerBlock;
+  const int n_chunks = (nt_count + kNtPerBlock - 1) / kNtPerBlock;
+  const int b = i / kBlock, t = i - b * kBlock;
+  const int panel = b / n_chunks, chunk = b - panel * n_chunks;
+  const int xcd = t % kXcds, local = t / kXcds;
+  mt = panel * (kXcds * kMtPerXcd) + xcd * kMtPerXcd + local % kMtPerXcd;
+  nt = chunk * kNtPerBlock + local / kMtPerXcd;
+  return mt < mt_bound && nt < nt_count;
+}
+
+static int xcd_order_grid(int mt_bound, int nt_count) {
+  const int n_chunks = (nt_count + kNtPerBlock - 1) / kNtPerBlock;
+  const int n_panels = (mt_bound + kXcds * kMtPerXcd - 1) / (kXcds * kMtPerXcd);
+  return n_panels * n_chunks * kXcds * kMtPerXcd * kNtPerBlock;
+}
+
 }  // namespace
 
 // XCD-aware order: the hardware hands workgroup i to XCD i % 8.  Remap so
@@ -123,10 +163,26 @@ constexpr uint32_t kOob = 0x80000000u;  // an offset past any num_records
 // lane) comes from two ds_read_b64_tr_b16 on the row-major B stage: within
 // each 16-lane group, lane i supplies the address of 4 consecutive n of row
 // (i / 4) and receives column i of that 4 x 16 block.
-constexpr int BM2 = 256, BN2 = 256, BK2 = 32;
-constexpr int kStages = 4;
-constexpr uint32_t kStageBytes = (BM2 + BN2) * BK2 * 2;     // 32 KiB
-constexpr size_t kSmem2 = (size_t)kStages * kStageBytes;    // 128 KiB
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+constexpr int BM2 = 256, BN2 = 256, BK2 = MOE_GEMM_BK;
+static_assert(BK2 == 32 || BK2 == 64, "BK must be 32 or 64");
+constexpr int kSub = BK2 / 16;                  // MFMA k-substeps per K-step
+constexpr int kDmaPerWave = BM2 * BK2 * 2 / 1024 / 4;  // per operand, per stage
+// 16-byte chunk swizzle of an A row (self-inverse in the chunk): BK = 32
+// rows hold 4 chunks, BK = 64 rows 8; both make the b128 reads of 16
+// consecutive rows at one logical chunk conflict-free.
+__device__ __forceinline__ int a_swz(int row, int chunk) {
+  return BK2 == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ (row & 7) ^ ((row >> 3) & 1);
+}
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 4
+#endif
+constexpr int kStages = MOE_GEMM_STAGES;
+constexpr uint32_t kStageBytes = (BM2 + BN2) * BK2 * 2;
+constexpr size_t kSmem2 = (size_t)kStages * kStageBytes;
+static_assert(kSmem2 <= 160 * 1024, "LDS ring exceeds 160 KiB");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -178,10 +234,14 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     int Kd, int N, int gelu) {
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
+  int mt, nt;
+#if MOE_GEMM_ORDER == 1
+  if (!decode_tile_xcd(blockIdx.x, mt_bound, nt_count, mt, nt)) return;
+#else
   const int logical = xcd_remap(blockIdx.x, mt_bound * nt_count);
   if (logical < 0) return;
-  int mt, nt;
   decode_tile(logical, mt_bound, nt_count, mt, nt);
+#endif
   int seg, row0, rows;
   if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
   // The lookup result is wave-uniform; keep it in scalar registers so the
@@ -201,11 +261,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
   // A: rows [row0, a_rows) of the buffer are addressable; rows past the
   // segment are read but their outputs never stored.
   const u32x4 ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
-  // instruction q of this wave covers rows 16*(4q + wave) .. +15
-  const int a_row_l = lane >> 2;                                    // + 16 * (4q + wave)
-  const int a_chunk = (lane & 3) ^ ((a_row_l >> 2) & 3);            // logical chunk of slot
-  const uint32_t a_off = (uint32_t)((a_row_l + 16 * wave) * Kd + a_chunk * 8) * 2;
-  const uint32_t a_qstride = (uint32_t)(64 * Kd) * 2;
+  // instruction q of this wave covers rows R*(4q + wave) .. +R-1, R = 1024 / (2 BK)
+  constexpr int kArows = 1024 / (BK2 * 2);
+  const int a_row_l = lane / (BK2 / 8);                             // + R * (4q + wave)
+  const int a_chunk = a_swz(a_row_l, lane % (BK2 / 8));             // q-invariant (R % 16 == 0 or 8)
+  const uint32_t a_off = (uint32_t)((a_row_l + kArows * wave) * Kd + a_chunk * 8) * 2;
+  const uint32_t a_qstride = (uint32_t)(4 * kArows * Kd) * 2;
   // B: this expert's slice from column n0 on; k rows past Kd are out of range.
   const u32x4 rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
   // instruction q of this wave covers k rows 2*(4q + wave) .. +1
@@ -220,21 +281,21 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt % kStages) * kStageBytes);
     const bool kok = k0 + a_chunk * 8 < Kd;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kDmaPerWave; ++q)
       dma_load16(st + (4 * q + wave) * 1024, kok ? a_off + q * a_qstride + (uint32_t)k0 * 2 : kOob,
                  ra_src);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kDmaPerWave; ++q)
       dma_load16(st + BM2 * BK2 * 2 + (4 * q + wave) * 1024,
                  b_off + q * b_qstride + (uint32_t)k0 * N * 2, rb_src);
   };
 
   // ---- LDS -> register operand addresses (relative to a stage) ----
   // A fragment i, substep ks: row wm*128 + i*32 + rr, chunk 2ks + kh.
-  uint32_t a_rd[2];
+  uint32_t a_rd[kSub];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    a_rd[ks] = (uint32_t)(wm * 128 + rr) * 64 + (uint32_t)(((2 * ks + kh) ^ ((rr >> 2) & 3)) * 16);
+  for (int ks = 0; ks < kSub; ++ks)
+    a_rd[ks] = (uint32_t)(wm * 128 + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
   // B^T fragment j: lane group g = lane/16, i = lane%16 reads k row
   // (g>>1)*8 + i/4 (+4 for the high half, +16 per substep) at n =
   // wn*128 + j*32 + (g&1)*16 + 4*(i%4).
@@ -256,31 +317,72 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = (Kd + BK2 - 1) / BK2;
-  // prologue: stages 0 .. kStages-2 in flight
+  // Operand fragments of one k-substep (16 k): 4 A (b128) + 4 B^T (2 x tr).
+  auto read_ops = [&](uint32_t st, int ks, bf16x8* a, bf16x8* b) {
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wave's loads of step kt are done once at most (kStages-2) later
-    // stages' 8 instructions each are still outstanding
-    wait_vmcnt<(kStages - 2) * 8>();
-    block_barrier();  // every wave's step-kt data in LDS; step kt-1 fully consumed
-    issue(kt + kStages - 1);  // refills the slot of step kt-1 (past K: zeros)
-    const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
+    for (int i = 0; i < 4; ++i) a[i] = lds_read_b128(st + a_rd[ks] + i * 32 * BK2 * 2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 a[4], b[4];
+    for (int j = 0; j < 4; ++j)
+      b[j] = lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+  };
+  auto mma = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_read_b128(st + a_rd[ks] + i * 2048);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  // 12 LDS reads spread between 16 MFMAs (mask 0x008 MFMA, 0x100 DS read).
+  auto interleave = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < 12; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  // Software pipeline, one barrier per K-step, placed mid-step:
+  //   [read substep-1 operands (Q) of step kt | MFMAs of substep 0 (P)]
+  //   wait for step kt+1's loads; barrier
+  //   issue loads of step kt+3 into the slot of step kt-1
+  //   [read substep-0 operands (P) of step kt+1 | MFMAs of substep 1 (Q)]
+  // so every LDS read has a substep of MFMA work to land behind.
+  const int KT = (Kd + BK2 - 1) / BK2;
+  // Ring: step kt lives in slot kt % kStages.  Iteration kt refills slot
+  // (kt-1) % kStages with step kt+kStages-1: every wave read that slot before
+  // the previous iteration's barrier.  The barrier sits before the last
+  // substep: it waits for step kt+1 (this wave's loads, then every wave's),
+  // after which the next step's first operands are read while the last
+  // substep's MFMAs run.  With 3+ stages the refill is issued right after the
+  // barrier (overlapping MFMAs); with 2 it must precede the wait.
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  for (int s = 0; s < kStages - 1; ++s) issue(s);
+  wait_vmcnt<(kStages - 2) * 2 * kDmaPerWave>();
+  block_barrier();
+  bf16x8 pa[4], pb[4], qa[4], qb[4];
+  read_ops(lds0, 0, pa, pb);
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
+    const uint32_t st1 = lds0 + (uint32_t)((kt + 1) % kStages) * kStageBytes;
+    if (kStages < 3) issue(kt + kStages - 1);  // past K: zeros into a slot that is never read
+#pragma unroll
+    for (int ks = 0; ks < kSub; ++ks) {
+      // operands of substep ks are in P (even ks) or Q (odd ks); read the
+      // next substep's into the other set while this one's MFMAs run
+      bf16x8* na = (ks & 1) ? pa : qa;
+      bf16x8* nb = (ks & 1) ? pb : qb;
+      if (ks + 1 < kSub) {
+        read_ops(st, ks + 1, na, nb);
+      } else {
+        wait_vmcnt<(kStages - 2) * 2 * kDmaPerWave>();  // step kt+1 landed here
+        block_barrier();                                 // ... and in every wave
+        // with 3+ stages the refill goes here, overlapping the last MFMAs
+        if (kStages >= 3) issue(kt + kStages - 1);
+        read_ops(st1, 0, na, nb);  // past the last step: harmless reads
+      }
+      if (ks & 1) mma(qa, qb); else mma(pa, pb);
+      interleave();
     }
   }
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
@@ -387,7 +489,11 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   const int ntc = (a.N + BN2 - 1) / BN2;
   const long long n_logical = (long long)mtb * ntc;
   if (n_logical <= 0) return hipSuccess;
+#if MOE_GEMM_ORDER == 1
+  const long long grid = xcd_order_grid(mtb, ntc);
+#else
   const long long grid = (n_logical + 7) / 8 * 8;
+#endif
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k_grouped_gemm_bf16<<<(unsigned)grid, 256, kSmem2, st>>>(
       (const bf16*)a.A, (const bf16*)a.B, (bf16*)a.C, a.offsets, a.G, a.fixed_rows,
