@@ -176,6 +176,9 @@ constexpr int kDmaPerWave = BM2 * BK2 * 2 / 1024 / 4;  // per operand, per stage
 __device__ __forceinline__ int a_swz(int row, int chunk) {
   return BK2 == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ (row & 7) ^ ((row >> 3) & 1);
 }
+#ifndef MOE_GEMM_SPREAD_DMA
+#define MOE_GEMM_SPREAD_DMA 1
+#endif
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 4
 #endif
@@ -332,6 +335,30 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
+#if MOE_GEMM_SPREAD_DMA
+  // The last substep's MFMAs with the refill loads of step kt+kStages-1
+  // spread between them (one DMA after every 16 / (2 kDmaPerWave) MFMAs).
+  auto mma_dma = [&](const bf16x8* a, const bf16x8* b, int kt_fill) {
+    const int k0 = kt_fill * BK2;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt_fill % kStages) * kStageBytes);
+    const bool kok = k0 + a_chunk * 8 < Kd;
+    constexpr int every = 16 / (2 * kDmaPerWave);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      if (t % every == every - 1) {
+        const int d = t / every;  // 0 .. 2*kDmaPerWave-1
+        if (d < kDmaPerWave)
+          dma_load16(st + (4 * d + wave) * 1024,
+                     kok ? a_off + d * a_qstride + (uint32_t)k0 * 2 : kOob, ra_src);
+        else
+          dma_load16(st + BM2 * BK2 * 2 + (4 * (d - kDmaPerWave) + wave) * 1024,
+                     b_off + (d - kDmaPerWave) * b_qstride + (uint32_t)k0 * N * 2, rb_src);
+      }
+    }
+  };
+#endif
   // 12 LDS reads spread between 16 MFMAs (mask 0x008 MFMA, 0x100 DS read).
   auto interleave = [&]() {
 #pragma unroll
@@ -377,10 +404,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
       } else {
         wait_vmcnt<(kStages - 2) * 2 * kDmaPerWave>();  // step kt+1 landed here
         block_barrier();                                 // ... and in every wave
+#if !MOE_GEMM_SPREAD_DMA
         // with 3+ stages the refill goes here, overlapping the last MFMAs
         if (kStages >= 3) issue(kt + kStages - 1);
+#endif
         read_ops(st1, 0, na, nb);  // past the last step: harmless reads
       }
+#if MOE_GEMM_SPREAD_DMA
+      if (kStages >= 3 && ks + 1 == kSub) {
+        if (ks & 1) mma_dma(qa, qb, kt + kStages - 1); else mma_dma(pa, pb, kt + kStages - 1);
+        continue;
+      }
+#endif
       if (ks & 1) mma(qa, qb); else mma(pa, pb);
       interleave();
     }
