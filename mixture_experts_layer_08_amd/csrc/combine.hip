@@ -100,13 +100,17 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ out,
   }
 }
 
+#ifndef MOE_COMBINE_VPL
+#define MOE_COMBINE_VPL 8
+#endif
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int nvec = a.H * (a.bf16 ? 2 : 4) / 16;
   const int grid = (a.T + 3) / 4;
   if (a.bf16)
-    k_combine<true, 4><<<grid, 256, 0, st>>>((const u32x4*)a.out, a.row_of, a.topk_w,
-                                             (const u32x4*)a.shared_out, (u32x4*)a.y, a.T, nvec,
-                                             a.K);
+    k_combine<true, MOE_COMBINE_VPL><<<grid, 256, 0, st>>>(
+        (const u32x4*)a.out, a.row_of, a.topk_w, (const u32x4*)a.shared_out, (u32x4*)a.y, a.T,
+        nvec, a.K);
   else
     k_combine<false, 4><<<grid, 256, 0, st>>>((const u32x4*)a.out, a.row_of, a.topk_w,
                                               (const u32x4*)a.shared_out, (u32x4*)a.y, a.T,
@@ -115,29 +119,44 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
 }
 
 // aux = E * sum_e (count_e / (T K)) (P_e) with P_e = (1/T) sum_t p[t,e].
-// One workgroup; thread e reduces its expert's per-block partials in block
-// order (fp64), thread 0 adds the per-expert terms in expert order.
+// One workgroup of 256 threads.  Expert e's per-block partials are split over
+// G = 256 / E_pad threads (E_pad = E rounded up to a power of two): thread
+// (e, g) sums blocks g, g+G, g+2G, ... in order (fp64), then a fixed-shape
+// tree over g combines them, and thread 0 adds the per-expert terms in
+// expert order.  Deterministic: every sum has a fixed order.
 __global__ __launch_bounds__(256) void k_aux(const int32_t* __restrict__ hist,
                                              const float* __restrict__ psum,
                                              float* __restrict__ aux, int T, int E, int K,
                                              int nblk) {
-  __shared__ double s_term[256];
-  const int e = threadIdx.x;
-  double term = 0.0;
+  __shared__ double s_p[256];
+  __shared__ long long s_c[256];
+  int e_pad = 1;
+  while (e_pad < E) e_pad <<= 1;
+  const int G = 256 / e_pad;
+  const int tid = threadIdx.x;
+  const int e = tid / G, g = tid % G;
+  double P = 0.0;
+  long long cnt = 0;
   if (e < E) {
-    long long cnt = 0;
-    double P = 0.0;
-    for (int b = 0; b < nblk; ++b) {
+    for (int b = g; b < nblk; b += G) {
       cnt += hist[(size_t)e * nblk + b];
       P += (double)psum[(size_t)e * nblk + b];
     }
-    term = ((double)cnt / ((double)T * K)) * (P / (double)T);
   }
-  s_term[e] = term;
+  s_p[tid] = P;
+  s_c[tid] = cnt;
   __syncthreads();
-  if (e == 0) {
+  for (int w = G >> 1; w > 0; w >>= 1) {
+    if (g < w) {
+      s_p[tid] += s_p[tid + w];
+      s_c[tid] += s_c[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
     double s = 0.0;
-    for (int i = 0; i < E; ++i) s += s_term[i];
+    for (int i = 0; i < E; ++i)
+      s += ((double)s_c[i * G] / ((double)T * K)) * (s_p[i * G] / (double)T);
     *aux = (float)((double)E * s);
   }
 }

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void k_route_bf16(
   for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero8 = {};
   int k = 0;
-  constexpr int U = CT <= 4 ? 4 : (CT <= 8 ? 2 : 1);
+  // loads in flight per lane: enough bytes per wave to cover HBM latency
+  constexpr int U = CT <= 2 ? 16 : (CT <= 4 ? 8 : (CT <= 8 ? 4 : 2));
   for (; k + 32 * U <= H; k += 32 * U) {
     bf16x8 a[U];
 #pragma unroll
