@@ -9,14 +9,13 @@
 // (many thin per-expert GEMMs in one kernel).
 //
 // The bf16 kernel's design is described above k_grouped_gemm_bf16 below:
-// 256 x 256 x 32 tiles on four waves, a 4-stage LDS ring filled by direct
-// HBM->LDS loads, the N-contiguous weight operand read through LDS transpose
-// reads, and an epilogue with the optional GELU(tanh) straight from the
-// accumulators.  Segment lookup happens on the device from `offsets` (a
-// wave-wide prefix sum of per-segment tile counts); the grid is sized for the
-// worst case and surplus workgroups exit at once, so there is no host sync.
-#include <type_traits>
-
+// 256 x 256 x 32 tiles on eight waves (two per SIMD), a 4-stage LDS ring
+// filled by direct HBM->LDS loads, the N-contiguous weight operand read
+// through LDS transpose reads, and an epilogue with the optional GELU(tanh)
+// straight from the accumulators.  Segment lookup happens on the device from
+// `offsets` (a wave-wide prefix sum of per-segment tile counts); the grid is
+// sized for the worst case and surplus workgroups exit at once, so there is
+// no host sync.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,27 +23,13 @@ namespace moe {
 
 namespace {
 
+// M-tiles per group of the tile order: consecutive workgroups sweep the
+// N-tiles of kGroupM M-tiles, so a group's A rows and the swept B columns
+// are re-read from L2 rather than HBM.
 #ifndef MOE_GEMM_GROUP_M
 #define MOE_GEMM_GROUP_M 4
 #endif
-#ifndef MOE_GEMM_XCD_REMAP
-#define MOE_GEMM_XCD_REMAP 0
-#endif
-// Tile order of the bf16 kernel: 0 = group-M sweep (decode_tile), 1 = XCD
-// panels (decode_tile_xcd).
-#ifndef MOE_GEMM_ORDER
-#define MOE_GEMM_ORDER 0
-#endif
-#ifndef MOE_GEMM_MT_PER_XCD
-#define MOE_GEMM_MT_PER_XCD 4
-#endif
-#ifndef MOE_GEMM_NT_PER_BLOCK
-#define MOE_GEMM_NT_PER_BLOCK 8
-#endif
 constexpr int kGroupM = MOE_GEMM_GROUP_M;
-constexpr int kXcds = 8;
-constexpr int kMtPerXcd = MOE_GEMM_MT_PER_XCD;
-constexpr int kNtPerBlock = MOE_GEMM_NT_PER_BLOCK;
 
 // Finds the segment of global M-tile `mt`.  Wave-uniform result (every wave
 // of the workgroup computes the same), so an early exit is workgroup-uniform.
@@ -99,63 +84,26 @@ __device__ __forceinline__ void decode_tile(int tile, int mt_bound, int nt_count
   nt = in_g / gsize;
 }
 
-// XCD panels.  The hardware hands workgroup i to XCD i % 8.  Workgroups are
-// taken in blocks of 8 * kMtPerXcd * kNtPerBlock: block b covers M-tiles
-// [P*8*kMtPerXcd, +8*kMtPerXcd) of panel P and N-tiles [c*kNtPerBlock,
-// +kNtPerBlock) of chunk c (panel-major), and inside a block XCD x owns M-tiles
-// x*kMtPerXcd .. +kMtPerXcd-1 against all the block's N-tiles.  So each XCD's
-// L2 holds a few A row blocks and the block's B column blocks, and every XCD
-// reads the same B blocks at the same time (shared through the Infinity
-// Cache).  Returns false for slots outside the tile grid.
-__device__ __forceinline__ bool decode_tile_xcd(int i, int mt_bound, int nt_count, int& mt,
-                                                int& nt) {
-  constexpr int kBlock = kXcds * kMtPerXcd * kNtPerBlock;
-  const int n_chunks = (nt_count + kNtPerBlock - 1) / kNtPerBlock;
-  const int b = i / kBlock, t = i - b * kBlock;
-  const int panel = b / n_chunks, chunk = b - panel * n_chunks;
-  const int xcd = t % kXcds, local = t / kXcds;
-  mt = panel * (kXcds * kMtPerXcd) + xcd * kMtPerXcd + local % kMtPerXcd;
-  nt = chunk * kNtPerBlock + local / kMtPerXcd;
-  return mt < mt_bound && nt < nt_count;
-}
-
-static int xcd_order_grid(int mt_bound, int nt_count) {
-  const int n_chunks = (nt_count + kNtPerBlock - 1) / kNtPerBlock;
-  const int n_panels = (mt_bound + kXcds * kMtPerXcd - 1) / (kXcds * kMtPerXcd);
-  return n_panels * n_chunks * kXcds * kMtPerXcd * kNtPerBlock;
-}
-
 }  // namespace
-
-// XCD-aware order: the hardware hands workgroup i to XCD i % 8.  Remap so
-// that each XCD walks a contiguous range of logical tiles, which the group-M
-// order turns into a compact block of (M-tile, N-tile) pairs sharing A rows
-// and B columns in that XCD's L2.  Returns -1 for padding workgroups.
-__device__ __forceinline__ int xcd_remap(int i, int n_logical) {
-  constexpr int kXcd = 8;
-  if (!MOE_GEMM_XCD_REMAP) return i < n_logical ? i : -1;
-  const int per = (n_logical + kXcd - 1) / kXcd;
-  const int l = (i % kXcd) * per + i / kXcd;
-  return l < n_logical ? l : -1;
-}
-
 
 constexpr uint32_t kOob = 0x80000000u;  // an offset past any num_records
 
-// 256 x 256 tile, BK = 32, 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4
-// MFMA 32x32x16 tiles (256 fp32 accumulators per lane, in AGPRs).
+// 256 x 256 x 32 tile on 8 waves in 2 (M) x 4 (N); each wave owns a 128 x 64
+// block = 4 x 2 MFMA 32x32x16 tiles (128 fp32 accumulators per lane).  Two
+// waves share each SIMD, so one wave's MFMAs run while the other is held at
+// a load issue, an LDS read or the barrier.
 //
 // Both operands go from HBM/L2 straight into LDS (buffer_load_dwordx4 ...
-// lds, no register staging) through a ring of kStages stages, each K-step's
-// loads issued kStages-1 steps before it is consumed, so that an L2 miss is
-// hidden behind several steps of MFMA work.  One s_barrier per K-step; the
-// wait for a stage's loads is an explicit vmcnt.
+// lds, no register staging) through a ring of kStages stages; step kt's loads
+// are issued while step kt-kStages+1 is multiplied, so an L2 miss is hidden
+// behind several steps of MFMA work.  One s_barrier per K-step; the wait for
+// a stage's loads is an explicit vmcnt.
 //
 // LDS stage (32 KiB): A [256 m][32 k] (64-byte rows, 16-byte chunk c stored
 // at c ^ ((m >> 2) & 3)) then B [32 k][256 n] (512-byte rows, 16-byte chunk c
 // stored at c ^ (4 * (k & 3))).  Each LDS-direct instruction of a wave fills
 // 1 KiB in lane order; a lane fetches the global chunk that the swizzle maps
-// to its slot.
+// to its slot.  Both swizzles make the fragment reads below conflict-free.
 //
 // The MFMA runs with the operands swapped (B^T fragment as "A"), so each lane
 // accumulates C^T: per 32x32 tile it owns row m = lane%32 and columns
@@ -163,26 +111,16 @@ constexpr uint32_t kOob = 0x80000000u;  // an offset past any num_records
 // lane) comes from two ds_read_b64_tr_b16 on the row-major B stage: within
 // each 16-lane group, lane i supplies the address of 4 consecutive n of row
 // (i / 4) and receives column i of that 4 x 16 block.
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
-#endif
-constexpr int BM2 = 256, BN2 = 256, BK2 = MOE_GEMM_BK;
-static_assert(BK2 == 32 || BK2 == 64, "BK must be 32 or 64");
-constexpr int kSub = BK2 / 16;                  // MFMA k-substeps per K-step
-constexpr int kDmaPerWave = BM2 * BK2 * 2 / 1024 / 4;  // per operand, per stage
-// 16-byte chunk swizzle of an A row (self-inverse in the chunk): BK = 32
-// rows hold 4 chunks, BK = 64 rows 8; both make the b128 reads of 16
-// consecutive rows at one logical chunk conflict-free.
-__device__ __forceinline__ int a_swz(int row, int chunk) {
-  return BK2 == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ (row & 7) ^ ((row >> 3) & 1);
-}
-#ifndef MOE_GEMM_SPREAD_DMA
-#define MOE_GEMM_SPREAD_DMA 1
-#endif
+constexpr int BM2 = 256, BN2 = 256, BK2 = 32;
+constexpr int kGemmThreads = 512;
+constexpr int kSub = BK2 / 16;  // MFMA k-substeps per K-step
+constexpr int kDma = 2;         // LDS-direct loads per operand, per wave, per stage
+__device__ __forceinline__ int a_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 4
 #endif
 constexpr int kStages = MOE_GEMM_STAGES;
+static_assert(kStages >= 3, "the refill of a stage is issued after the barrier of the step before");
 constexpr uint32_t kStageBytes = (BM2 + BN2) * BK2 * 2;
 constexpr size_t kSmem2 = (size_t)kStages * kStageBytes;
 static_assert(kSmem2 <= 160 * 1024, "LDS ring exceeds 160 KiB");
@@ -207,6 +145,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Raw buffer descriptor (dwords: base lo, base hi, num_records, format) for
@@ -231,20 +170,15 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
 }
 #pragma clang diagnostic pop
 
-__global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C,
     const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows, int mt_bound,
     int Kd, int N, int gelu) {
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
+  if ((int)blockIdx.x >= mt_bound * nt_count) return;
   int mt, nt;
-#if MOE_GEMM_ORDER == 1
-  if (!decode_tile_xcd(blockIdx.x, mt_bound, nt_count, mt, nt)) return;
-#else
-  const int logical = xcd_remap(blockIdx.x, mt_bound * nt_count);
-  if (logical < 0) return;
-  decode_tile(logical, mt_bound, nt_count, mt, nt);
-#endif
+  decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
   int seg, row0, rows;
   if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
   // The lookup result is wave-uniform; keep it in scalar registers so the
@@ -255,42 +189,41 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int rr = lane & 31, kh = lane >> 5;
   const int n0 = nt * BN2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // ---- global -> LDS loaders (4 + 4 instructions per wave per stage) ----
-  // A: rows [row0, a_rows) of the buffer are addressable; rows past the
-  // segment are read but their outputs never stored.
+  // ---- global -> LDS loaders (2 + 2 instructions per wave per stage) ----
+  // A: instruction d of this wave covers stage rows 16*(8d + wave) .. +15,
+  // four lanes per 64-byte row.  Rows [row0, a_rows) are addressable; rows
+  // past the segment are read but their outputs never stored.
   const u32x4 ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
-  // instruction q of this wave covers rows R*(4q + wave) .. +R-1, R = 1024 / (2 BK)
-  constexpr int kArows = 1024 / (BK2 * 2);
-  const int a_row_l = lane / (BK2 / 8);                             // + R * (4q + wave)
-  const int a_chunk = a_swz(a_row_l, lane % (BK2 / 8));             // q-invariant (R % 16 == 0 or 8)
-  const uint32_t a_off = (uint32_t)((a_row_l + kArows * wave) * Kd + a_chunk * 8) * 2;
-  const uint32_t a_qstride = (uint32_t)(4 * kArows * Kd) * 2;
-  // B: this expert's slice from column n0 on; k rows past Kd are out of range.
+  const int a_row_l = lane >> 2;
+  const int a_chunk = a_swz(a_row_l, lane & 3);  // (row >> 2) & 3 is d- and wave-invariant
+  const uint32_t a_off = (uint32_t)((a_row_l + 16 * wave) * Kd + a_chunk * 8) * 2;
+  const uint32_t a_dstride = (uint32_t)(8 * 16 * Kd) * 2;
+  // B: this expert's slice from column n0 on; instruction d of this wave
+  // covers k rows 2*(8d + wave) .. +1, 32 lanes per 512-byte row.  k rows
+  // past Kd lie beyond num_records and read as zero.
   const u32x4 rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
-  // instruction q of this wave covers k rows 2*(4q + wave) .. +1
-  const int b_row_l = lane >> 5;                                    // + 2 * (4q + wave)
-  const int b_row0 = b_row_l + 2 * wave;                            // (row & 3) is q-invariant
+  const int b_row0 = (lane >> 5) + 2 * wave;               // (row & 3) is d-invariant
   const int b_chunk = (lane & 31) ^ (4 * (b_row0 & 3));
   const uint32_t b_off = (uint32_t)(b_row0 * N + b_chunk * 8) * 2;
-  const uint32_t b_qstride = (uint32_t)(8 * N) * 2;
+  const uint32_t b_dstride = (uint32_t)(16 * N) * 2;
 
-  auto issue = [&](int kt) {
+  // load d (0, 1: A; 2, 3: B) of step kt into the stage at LDS address st
+  auto dma = [&](uint32_t st, int d, int kt) {
     const int k0 = kt * BK2;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt % kStages) * kStageBytes);
-    const bool kok = k0 + a_chunk * 8 < Kd;
-#pragma unroll
-    for (int q = 0; q < kDmaPerWave; ++q)
-      dma_load16(st + (4 * q + wave) * 1024, kok ? a_off + q * a_qstride + (uint32_t)k0 * 2 : kOob,
-                 ra_src);
-#pragma unroll
-    for (int q = 0; q < kDmaPerWave; ++q)
-      dma_load16(st + BM2 * BK2 * 2 + (4 * q + wave) * 1024,
-                 b_off + q * b_qstride + (uint32_t)k0 * N * 2, rb_src);
+    if (d < kDma)
+      dma_load16(st + (8 * d + wave) * 1024,
+                 k0 + a_chunk * 8 < Kd ? a_off + d * a_dstride + (uint32_t)k0 * 2 : kOob, ra_src);
+    else
+      dma_load16(st + BM2 * BK2 * 2 + (8 * (d - kDma) + wave) * 1024,
+                 b_off + (d - kDma) * b_dstride + (uint32_t)k0 * N * 2, rb_src);
+  };
+  auto stage_addr = [&](int kt) {
+    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt % kStages) * kStageBytes);
   };
 
   // ---- LDS -> register operand addresses (relative to a stage) ----
@@ -301,124 +234,89 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     a_rd[ks] = (uint32_t)(wm * 128 + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
   // B^T fragment j: lane group g = lane/16, i = lane%16 reads k row
   // (g>>1)*8 + i/4 (+4 for the high half, +16 per substep) at n =
-  // wn*128 + j*32 + (g&1)*16 + 4*(i%4).
+  // wn*64 + j*32 + (g&1)*16 + 4*(i%4).
   const int bg = lane >> 4, bi = lane & 15;
   const int b_krow = (bg >> 1) * 8 + (bi >> 2);
-  uint32_t b_rd[4];
+  uint32_t b_rd[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = wn * 128 + j * 32 + (bg & 1) * 16 + 4 * (bi & 3);
+  for (int j = 0; j < 2; ++j) {
+    const int n = wn * 64 + j * 32 + (bg & 1) * 16 + 4 * (bi & 3);
     const int chunk = (n >> 3) ^ (4 * (b_krow & 3));
     b_rd[j] = BM2 * BK2 * 2 + (uint32_t)b_krow * 512 + (uint32_t)chunk * 16 + (uint32_t)(n & 7) * 2;
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Operand fragments of one k-substep (16 k): 4 A (b128) + 4 B^T (2 x tr).
+  // Operand fragments of one k-substep (16 k): 4 A (b128) + 2 B^T (2 x tr).
   auto read_ops = [&](uint32_t st, int ks, bf16x8* a, bf16x8* b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = lds_read_b128(st + a_rd[ks] + i * 32 * BK2 * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       b[j] = lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
   };
-  auto mma = [&](const bf16x8* a, const bf16x8* b) {
+  // 8 LDS reads spread between 8 MFMAs (mask 0x008 MFMA, 0x100 DS read).
+  auto mma_reads = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  };
-#if MOE_GEMM_SPREAD_DMA
-  // The last substep's MFMAs with the refill loads of step kt+kStages-1
-  // spread between them (one DMA after every 16 / (2 kDmaPerWave) MFMAs).
-  auto mma_dma = [&](const bf16x8* a, const bf16x8* b, int kt_fill) {
-    const int k0 = kt_fill * BK2;
-    const uint32_t st = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt_fill % kStages) * kStageBytes);
-    const bool kok = k0 + a_chunk * 8 < Kd;
-    constexpr int every = 16 / (2 * kDmaPerWave);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = t >> 2, j = t & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-      if (t % every == every - 1) {
-        const int d = t / every;  // 0 .. 2*kDmaPerWave-1
-        if (d < kDmaPerWave)
-          dma_load16(st + (4 * d + wave) * 1024,
-                     kok ? a_off + d * a_qstride + (uint32_t)k0 * 2 : kOob, ra_src);
-        else
-          dma_load16(st + BM2 * BK2 * 2 + (4 * (d - kDmaPerWave) + wave) * 1024,
-                     b_off + (d - kDmaPerWave) * b_qstride + (uint32_t)k0 * N * 2, rb_src);
-      }
-    }
-  };
-#endif
-  // 12 LDS reads spread between 16 MFMAs (mask 0x008 MFMA, 0x100 DS read).
-  auto interleave = [&]() {
-#pragma unroll
-    for (int t = 0; t < 12; ++t) {
+    for (int t = 0; t < 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+  // The last substep's MFMAs with the refill loads of step kt_fill between
+  // them (one after every second MFMA).
+  auto mma_refill = [&](const bf16x8* a, const bf16x8* b, int kt_fill) {
+    const uint32_t st = stage_addr(kt_fill);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = t >> 1, j = t & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      if (t & 1) dma(st, t >> 1, kt_fill);
+    }
   };
 
-  // Software pipeline, one barrier per K-step, placed mid-step:
-  //   [read substep-1 operands (Q) of step kt | MFMAs of substep 0 (P)]
-  //   wait for step kt+1's loads; barrier
-  //   issue loads of step kt+3 into the slot of step kt-1
-  //   [read substep-0 operands (P) of step kt+1 | MFMAs of substep 1 (Q)]
-  // so every LDS read has a substep of MFMA work to land behind.
-  const int KT = (Kd + BK2 - 1) / BK2;
+  // Software pipeline, one barrier per K-step (BK = 32 = two substeps):
+  //   read substep-1 operands (Q) of step kt  | MFMAs of substep 0 (P)
+  //   wait: step kt+1's loads landed (own), own LDS reads done; barrier
+  //   read substep-0 operands (P) of step kt+1 | MFMAs of substep 1 (Q),
+  //                                              refill step kt+kStages-1
   // Ring: step kt lives in slot kt % kStages.  Iteration kt refills slot
-  // (kt-1) % kStages with step kt+kStages-1: every wave read that slot before
-  // the previous iteration's barrier.  The barrier sits before the last
-  // substep: it waits for step kt+1 (this wave's loads, then every wave's),
-  // after which the next step's first operands are read while the last
-  // substep's MFMAs run.  With 3+ stages the refill is issued right after the
-  // barrier (overlapping MFMAs); with 2 it must precede the wait.
+  // (kt-1) % kStages, whose last reads every wave completed before this
+  // iteration's barrier.  At the wait of iteration kt this wave has issued
+  // steps up to kt+kStages-2, so allowing kStages-3 steps in flight means
+  // step kt+1 has landed; after the barrier it has landed for every wave.
+  const int KT = (Kd + BK2 - 1) / BK2;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s);
-  wait_vmcnt<(kStages - 2) * 2 * kDmaPerWave>();
-  block_barrier();
-  bf16x8 pa[4], pb[4], qa[4], qb[4];
+  for (int s = 0; s < kStages - 1; ++s) {
+    const uint32_t st = stage_addr(s);
+#pragma unroll
+    for (int d = 0; d < 2 * kDma; ++d) dma(st, d, s);
+  }
+  wait_vmcnt<(kStages - 2) * 2 * kDma>();  // step 0 landed (own loads)
+  block_barrier();                          // ... and every wave's
+  bf16x8 pa[4], pb[2], qa[4], qb[2];
   read_ops(lds0, 0, pa, pb);
   for (int kt = 0; kt < KT; ++kt) {
     const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
     const uint32_t st1 = lds0 + (uint32_t)((kt + 1) % kStages) * kStageBytes;
-    if (kStages < 3) issue(kt + kStages - 1);  // past K: zeros into a slot that is never read
-#pragma unroll
-    for (int ks = 0; ks < kSub; ++ks) {
-      // operands of substep ks are in P (even ks) or Q (odd ks); read the
-      // next substep's into the other set while this one's MFMAs run
-      bf16x8* na = (ks & 1) ? pa : qa;
-      bf16x8* nb = (ks & 1) ? pb : qb;
-      if (ks + 1 < kSub) {
-        read_ops(st, ks + 1, na, nb);
-      } else {
-        wait_vmcnt<(kStages - 2) * 2 * kDmaPerWave>();  // step kt+1 landed here
-        block_barrier();                                 // ... and in every wave
-#if !MOE_GEMM_SPREAD_DMA
-        // with 3+ stages the refill goes here, overlapping the last MFMAs
-        if (kStages >= 3) issue(kt + kStages - 1);
-#endif
-        read_ops(st1, 0, na, nb);  // past the last step: harmless reads
-      }
-#if MOE_GEMM_SPREAD_DMA
-      if (kStages >= 3 && ks + 1 == kSub) {
-        if (ks & 1) mma_dma(qa, qb, kt + kStages - 1); else mma_dma(pa, pb, kt + kStages - 1);
-        continue;
-      }
-#endif
-      if (ks & 1) mma(qa, qb); else mma(pa, pb);
-      interleave();
-    }
+    read_ops(st, 1, qa, qb);
+    mma_reads(pa, pb);
+    wait_vmcnt<(kStages - 3) * 2 * kDma>();
+    wait_lgkm0();
+    block_barrier();
+    read_ops(st1, 0, pa, pb);  // past the last step: harmless reads of a landed stage
+    mma_refill(qa, qb, kt + kStages - 1);  // past K: zeros into a slot never read
   }
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 
@@ -430,10 +328,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm_bf16(
     if (m >= rows) continue;
     bf16* crow = C + (size_t)(row0 + m) * N;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + j * 32 + 8 * g + 4 * kh;
+        const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * kh;
         if (n < N) {
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
@@ -522,15 +420,10 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st) {
   }
   const int mtb = mt_bound_for(a, BM2);
   const int ntc = (a.N + BN2 - 1) / BN2;
-  const long long n_logical = (long long)mtb * ntc;
-  if (n_logical <= 0) return hipSuccess;
-#if MOE_GEMM_ORDER == 1
-  const long long grid = xcd_order_grid(mtb, ntc);
-#else
-  const long long grid = (n_logical + 7) / 8 * 8;
-#endif
+  const long long grid = (long long)mtb * ntc;
+  if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_grouped_gemm_bf16<<<(unsigned)grid, 256, kSmem2, st>>>(
+  k_grouped_gemm_bf16<<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
       (const bf16*)a.A, (const bf16*)a.B, (bf16*)a.C, a.offsets, a.G, a.fixed_rows,
       a.offsets ? a.max_rows : a.fixed_rows, mtb, a.Kd, a.N, a.gelu);
   return hipGetLastError();
