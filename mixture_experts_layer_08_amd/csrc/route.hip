@@ -8,13 +8,22 @@
 //
 // One workgroup of 256 threads handles a route block of kRouteBlock = 64
 // tokens.  bf16 mode runs the router GEMM on MFMA (v_mfma_f32_16x16x32_bf16):
-// each wave owns 16 tokens and all experts, reading its x rows straight from
-// HBM into the A operand (16 contiguous bytes per lane) and the transposed
-// router weight (wT [E_pad][H], L2-resident) as the B operand.  fp32 mode
-// uses plain FMA.  The epilogue puts the block's logits in LDS, then
-//   - one thread per token selects the top-k, computes softmax and weights;
-//   - one thread per expert sums the block's probabilities (fixed token
-//     order) and ranks the block's assignments to it in token order.
+// each wave owns 16 tokens and all experts.  Its x rows stream from HBM
+// straight into the A operand through a ring of register slots, loads issued
+// R-1 MFMA steps ahead so that every wave keeps ~16-32 KiB in flight.  The
+// transposed router weight (wT [E_pad][H]) is staged in LDS chunk by chunk,
+// once per workgroup, double-buffered, and read from there as the B operand
+// by all four waves.  fp32 mode uses plain FMA.
+//
+// The epilogue works on the block's fp32 logits in LDS:
+//   - four lanes per token select the top-k (K rounds of a 4-lane argmax;
+//     larger logit first, the lower expert index on equal logits), and
+//     compute the softmax and the renormalised weights;
+//   - each token ORs its bit into a 64-bit mask per chosen expert, so the
+//     in-block rank of (t, e) is the popcount of e's mask below bit t and
+//     the block histogram is the popcount of the whole mask (OR is
+//     order-independent: the result is deterministic);
+//   - one thread per expert sums the block's probabilities in token order.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,9 +42,11 @@ __global__ __launch_bounds__(256) void k_transpose_router(const bf16* __restrict
 }
 
 // Shared epilogue.  s_logit holds the block's fp32 logits, row stride ES.
-// Called by all 256 threads after a barrier that published s_logit.
-__device__ void route_epilogue(float* s_logit, int ES, int32_t* s_ids, int t0, int nt,
-                               int E, int K, int nblk, float* __restrict__ logits_out,
+// Called by all 256 threads after a barrier that published s_logit.  s_ids
+// is [kRouteBlock][8], s_mask [E] (scratch).
+__device__ void route_epilogue(float* s_logit, int ES, int32_t* s_ids,
+                               unsigned long long* s_mask, int t0, int nt, int E, int K,
+                               int nblk, float* __restrict__ logits_out,
                                int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                                int32_t* __restrict__ hist, float* __restrict__ psum,
                                int32_t* __restrict__ lrank) {
@@ -46,69 +57,104 @@ __device__ void route_epilogue(float* s_logit, int ES, int32_t* s_ids, int t0, i
       logits_out[(size_t)(t0 + t) * E + e] = s_logit[t * ES + e];
     }
   }
+  for (int e = tid; e < E; e += blockDim.x) s_mask[e] = 0ull;
   __syncthreads();
-  if (tid < nt) {
-    float* L = s_logit + tid * ES;
-    // Descending top-8 by insertion; equal values keep the earlier (lower)
-    // expert index first because the comparison is strict.
-    float bv[8];
-    int bi[8];
+
+  // ---- top-k, softmax, weights: lanes 4t .. 4t+3 handle token t ----
+  const int tok = tid >> 2, sub = tid & 3;  // the 4 lanes of a token are adjacent
+  float* L = s_logit + tok * ES;
+  const bool tok_ok = tok < nt;  // uniform over the 4 lanes of a token
+  float bv[8];
+  int bi[8];
+  unsigned long long taken = 0;  // bit i: expert sub + 4i already chosen
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { bv[j] = -INFINITY; bi[j] = 0; }
-    for (int e = 0; e < E; ++e) {
-      const float v = L[e];
-#pragma unroll
-      for (int j = 7; j > 0; --j) {
-        const bool shift = v > bv[j - 1];
-        const bool place = !shift && v > bv[j];
-        const float nv = shift ? bv[j - 1] : (place ? v : bv[j]);
-        const int ni = shift ? bi[j - 1] : (place ? e : bi[j]);
-        bv[j] = nv;
-        bi[j] = ni;
+  for (int j = 0; j < 8; ++j) {
+    bv[j] = -INFINITY;
+    bi[j] = 0;
+    if (j < K) {
+      float v = -INFINITY;
+      int ie = 0x7fffffff;
+      if (tok_ok) {
+        int i = 0;
+        for (int e = sub; e < E; e += 4, ++i) {
+          const float x = L[e];
+          // strict compare in increasing e: the lower index wins a tie
+          if (!((taken >> i) & 1ull) && (x > v || ie == 0x7fffffff)) {
+            v = x;
+            ie = e;
+          }
+        }
       }
-      if (v > bv[0]) { bv[0] = v; bi[0] = e; }
+#pragma unroll
+      for (int d = 1; d <= 2; d <<= 1) {
+        const float ov = __shfl_xor(v, d, kWave);
+        const int oe = __shfl_xor(ie, d, kWave);
+        if (ov > v || (ov == v && oe < ie)) {
+          v = ov;
+          ie = oe;
+        }
+      }
+      bv[j] = v;
+      bi[j] = ie;
+      if (tok_ok && (ie & 3) == sub) taken |= 1ull << (ie >> 2);
     }
+  }
+  if (tok_ok) {
     const float m = bv[0];
     float s = 0.0f;
-    for (int e = 0; e < E; ++e) {
-      const float z = __expf(L[e] - m);
-      L[e] = z;
-      s += z;
-    }
+    for (int e = sub; e < E; e += 4) s += __expf(L[e] - m);
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
     const float inv = 1.0f / s;
-    for (int e = 0; e < E; ++e) L[e] *= inv;   // probabilities, for the aux partial sums
-    float zsel[8];
-    float zs = 0.0f;
+    for (int e = sub; e < E; e += 4) L[e] = __expf(L[e] - m) * inv;  // probabilities
+    if (sub == 0) {
+      float zsel[8];
+      float zs = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      zsel[j] = j < K ? __expf(bv[j] - m) : 0.0f;
-      zs += zsel[j];
-    }
-    const size_t t = (size_t)(t0 + tid);
+      for (int j = 0; j < 8; ++j) {
+        zsel[j] = j < K ? __expf(bv[j] - m) : 0.0f;
+        zs += zsel[j];
+      }
+      const size_t t = (size_t)(t0 + tok);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < K) {
-        topk_ids[t * K + j] = bi[j];
-        topk_w[t * K + j] = zsel[j] / zs;
-        s_ids[tid * K + j] = bi[j];
+      for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+          topk_ids[t * K + j] = bi[j];
+          topk_w[t * K + j] = zsel[j] / zs;
+          s_ids[tok * 8 + j] = bi[j];
+          atomicOr(&s_mask[bi[j]], 1ull << tok);
+        }
       }
     }
   }
   __syncthreads();
+
+  // ---- per-block results for the aux loss and the permutation ----
   const int blk = blockIdx.x;
   for (int e = tid; e < E; e += blockDim.x) {
     float ps = 0.0f;
-    int cnt = 0;
-    for (int t = 0; t < nt; ++t) {
-      ps += s_logit[t * ES + e];
-      for (int j = 0; j < K; ++j) {
-        if (s_ids[t * K + j] == e) lrank[(size_t)(t0 + t) * K + j] = cnt++;
-      }
-    }
+    for (int t = 0; t < nt; ++t) ps += s_logit[t * ES + e];
     psum[(size_t)e * nblk + blk] = ps;
-    hist[(size_t)e * nblk + blk] = cnt;
+    hist[(size_t)e * nblk + blk] = __popcll(s_mask[e]);
+  }
+  for (int i = tid; i < nt * K; i += blockDim.x) {
+    const int t = i / K, j = i - t * K;
+    const unsigned long long below = (1ull << t) - 1ull;
+    lrank[(size_t)(t0 + t) * K + j] = __popcll(s_mask[s_ids[t * 8 + j]] & below);
   }
 }
+
+// k per staged weight chunk (16 KiB of bf16 weights per chunk, at most 512)
+// and the x ring depth in MFMA steps (a multiple of the steps per chunk).
+template <int CT>
+constexpr int route_kc() { return 8192 / (16 * CT) < 512 ? 8192 / (16 * CT) : 512; }
+template <int CT>
+constexpr int route_ring() { return CT <= 4 ? 32 : 16; }
+
+// Buffer-descriptor word 3 for raw 32-bit-indexed loads, and an offset past
+// any descriptor size used here (reads as zero).
+constexpr int kBufferFormat = 0x00020000;
+constexpr uint32_t kOffsetOob = 0x80000000u;
 
 template <int CT>
 __global__ __launch_bounds__(256) void k_route_bf16(
@@ -116,47 +162,105 @@ __global__ __launch_bounds__(256) void k_route_bf16(
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, float* __restrict__ psum, int32_t* __restrict__ lrank, int T,
     int H, int E, int K, int nblk) {
-  extern __shared__ float s_logit[];
+  extern __shared__ __attribute__((aligned(16))) float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
+  __shared__ unsigned long long s_mask[256];
+  constexpr int EP = 16 * CT;            // padded experts (rows of wT)
+  constexpr int KC = route_kc<CT>();     // k per weight chunk
+  constexpr int SPC = KC / 32;           // MFMA steps per chunk
+  constexpr int WROW = KC + 8;           // LDS row stride (elements): 16-byte pad
+  constexpr int WBUF = EP * WROW;        // elements per weight buffer
+  constexpr int WVEC = EP * KC / 8;      // 16-byte vectors per chunk
+  constexpr int WPT = WVEC / 256;        // per thread
+  constexpr int R = route_ring<CT>();    // x ring slots (MFMA steps in flight)
+  static_assert(WVEC % 256 == 0 && R % SPC == 0, "route tiling");
+  bf16* wbuf = (bf16*)s_logit;           // two weight buffers; later the logits tile
+
   const int ES = E | 1;
   const int t0 = blockIdx.x * kRouteBlock;
   const int nt = min(kRouteBlock, T - t0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = t0 + wave * 16 + (lane & 15);
-  const bool row_ok = row < T;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int kg = (lane >> 4) * 8;
-  const bf16* xr = x + (size_t)(row_ok ? row : 0) * H + kg;
-  const bf16* wr = wT + (size_t)(lane & 15) * H + kg;
+  const int nsteps = (H + 31) / 32;
+  const int nchunks = (H + KC - 1) / KC;
+  const int ngroups = (nsteps + R - 1) / R;
+
+  // All loads are buffer loads with no branch around them (a divergent
+  // branch would make the compiler wait for every load in flight): the
+  // descriptor's size bounds the rows (rows past T read as zero), and an
+  // offset past the size zeroes k past H.
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (size_t)t0 * H), (short)0, nt * H * 2, kBufferFormat);
+  const uint32_t xoff = (uint32_t)((wave * 16 + (lane & 15)) * H + kg) * 2;
+  auto xload = [&](int s) -> bf16x8 {
+    const uint32_t off = s * 32 + kg < H ? xoff + (uint32_t)s * 64 : kOffsetOob;
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
+  };
+  // weight chunk c: thread's vectors v = tid + 256 q -> row v / (KC/8),
+  // 8-element piece v % (KC/8); zero past H (H is a multiple of 8)
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wT, (short)0, EP * H * 2, kBufferFormat);
+  u32x4 wreg[WPT];
+  auto wload = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int v = tid + 256 * q;
+      const int r = v / (KC / 8), p = v % (KC / 8);
+      const int k = c * KC + p * 8;
+      const uint32_t off = k < H ? (uint32_t)(r * H + k) * 2 : kOffsetOob;
+      wreg[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+    }
+  };
+  auto wstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int v = tid + 256 * q;
+      const int r = v / (KC / 8), p = v % (KC / 8);
+      *(u32x4*)(wbuf + buf * WBUF + r * WROW + p * 8) = wreg[q];
+    }
+  };
+
   f32x4 acc[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8 zero8 = {};
-  int k = 0;
-  // loads in flight per lane: enough bytes per wave to cover HBM latency
-  constexpr int U = CT <= 2 ? 16 : (CT <= 4 ? 8 : (CT <= 8 ? 4 : 2));
-  for (; k + 32 * U <= H; k += 32 * U) {
-    bf16x8 a[U];
+  bf16x8 ring[R];
+  wload(0);
+  wstore(0);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      a[u] = row_ok ? *(const bf16x8*)(xr + k + 32 * u) : zero8;
+  for (int i = 0; i < R - 1; ++i) ring[i] = xload(i);
+  if (nchunks > 1) wload(1);
+  __syncthreads();
+  // B fragment of tile ct at step s_in of a chunk: row ct*16 + lane%16,
+  // 8 k from s_in*32 + 8*(lane/16).  The 16-byte row pad makes the 16 rows
+  // of one read fall in distinct banks.
+  const int b_off = (lane & 15) * WROW + kg;
+  // Whole groups of R steps: steps past the last one multiply zero rows of x.
+  for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int i = 0; i < R; ++i) {
+      const int s = g * R + i;
+      ring[(i + R - 1) % R] = xload(s + R - 1);
+      const int c = s / SPC;
+      // steps past the last chunk read the last chunk's buffer (finite
+      // weights times zero rows of x): the other buffer may never have been
+      // written, and stale LDS bits could be NaN
+      const bf16* wb = wbuf + (min(c, nchunks - 1) & 1) * WBUF + (i % SPC) * 32 + b_off;
 #pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const bf16x8 b = *(const bf16x8*)(wr + (size_t)c * 16 * H + k + 32 * u);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc[c], 0, 0, 0);
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 b = *(const bf16x8*)(wb + ct * 16 * WROW);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i], b, acc[ct], 0, 0, 0);
+      }
+      if ((i + 1) % SPC == 0 && c + 1 < nchunks) {  // uniform over the workgroup
+        // chunk c done: publish chunk c+1 into the other buffer, whose last
+        // reads (chunk c-1) every wave finished before the previous barrier
+        wstore((c + 1) & 1);
+        __syncthreads();
+        if (c + 2 < nchunks) wload(c + 2);
       }
     }
   }
-  for (; k < H; k += 32) {
-    const bool kin = k + kg < H;
-    const bf16x8 a = (row_ok && kin) ? *(const bf16x8*)(xr + k) : zero8;
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const bf16x8 b = kin ? *(const bf16x8*)(wr + (size_t)c * 16 * H + k) : zero8;
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-    }
-  }
+  __syncthreads();  // every wave is done with the weight buffers
   // D layout of the 16x16 tile: lane holds rows 4*(lane/16)+i, column lane%16.
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
@@ -171,8 +275,8 @@ __global__ __launch_bounds__(256) void k_route_bf16(
     }
   }
   __syncthreads();
-  route_epilogue(s_logit, ES, s_ids, t0, nt, E, K, nblk, logits, topk_ids, topk_w, hist, psum,
-                 lrank);
+  route_epilogue(s_logit, ES, s_ids, s_mask, t0, nt, E, K, nblk, logits, topk_ids, topk_w,
+                 hist, psum, lrank);
 }
 
 __global__ __launch_bounds__(256) void k_route_f32(
@@ -182,6 +286,7 @@ __global__ __launch_bounds__(256) void k_route_f32(
     int H, int E, int K, int nblk) {
   extern __shared__ float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
+  __shared__ unsigned long long s_mask[256];
   const int ES = E | 1;
   const int t0 = blockIdx.x * kRouteBlock;
   const int nt = min(kRouteBlock, T - t0);
@@ -193,8 +298,8 @@ __global__ __launch_bounds__(256) void k_route_f32(
     s_logit[t * ES + e] = acc + (bias ? bias[e] : 0.0f);
   }
   __syncthreads();
-  route_epilogue(s_logit, ES, s_ids, t0, nt, E, K, nblk, logits, topk_ids, topk_w, hist, psum,
-                 lrank);
+  route_epilogue(s_logit, ES, s_ids, s_mask, t0, nt, E, K, nblk, logits, topk_ids, topk_w,
+                 hist, psum, lrank);
 }
 
 // Routing from caller-given fp32 logits (no GEMM, logits not rewritten).
@@ -204,6 +309,7 @@ __global__ __launch_bounds__(256) void k_route_from_logits(
     int32_t* __restrict__ lrank, int T, int E, int K, int nblk) {
   extern __shared__ float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
+  __shared__ unsigned long long s_mask[256];
   const int ES = E | 1;
   const int t0 = blockIdx.x * kRouteBlock;
   const int nt = min(kRouteBlock, T - t0);
@@ -212,11 +318,19 @@ __global__ __launch_bounds__(256) void k_route_from_logits(
     s_logit[t * ES + e] = logits[(size_t)(t0 + t) * E + e];
   }
   __syncthreads();
-  route_epilogue(s_logit, ES, s_ids, t0, nt, E, K, nblk, nullptr, topk_ids, topk_w, hist, psum,
-                 lrank);
+  route_epilogue(s_logit, ES, s_ids, s_mask, t0, nt, E, K, nblk, nullptr, topk_ids, topk_w,
+                 hist, psum, lrank);
 }
 
 size_t route_lds_bytes(int E) { return (size_t)kRouteBlock * (E | 1) * sizeof(float); }
+
+// bf16 router: the two weight buffers or the fp32 logits tile, whichever is
+// larger (they share the space).
+template <int CT>
+static size_t route_bf16_lds_bytes(int E) {
+  const size_t wbufs = 2 * (size_t)(16 * CT) * (route_kc<CT>() + 8) * 2;
+  return std::max(wbufs, route_lds_bytes(E));
+}
 
 // Column tiles of 16 experts for the bf16 router: a power of two from 1 to 16
 // (rows of wT beyond E are zero and their logits are never stored).
@@ -225,13 +339,24 @@ int route_col_tiles(int E) {
   return ct <= 1 ? 1 : ct <= 2 ? 2 : ct <= 4 ? 4 : ct <= 8 ? 8 : 16;
 }
 
-// Dynamic LDS above 64 KiB (E > 248) must be allowed explicitly; gfx950 has
-// 160 KiB of LDS per workgroup.
+// Dynamic LDS above 64 KiB must be allowed explicitly; gfx950 has 160 KiB of
+// LDS per workgroup.
 template <typename F>
 static hipError_t allow_lds(F* kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)bytes);
+}
+
+template <int CT>
+static hipError_t launch_route_bf16(const RouteArgs& a, int nblk, hipStream_t st) {
+  const size_t lds = route_bf16_lds_bytes<CT>(a.E);
+  hipError_t err = allow_lds(k_route_bf16<CT>, lds);
+  if (err != hipSuccess) return err;
+  k_route_bf16<CT><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.wT, a.bias, a.logits,
+                                           a.topk_ids, a.topk_w, a.hist, a.psum, a.lrank, a.T,
+                                           a.H, a.E, a.K, nblk);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
@@ -258,24 +383,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     k_transpose_router<<<grid, 256, 0, st>>>((const bf16*)a.w_r, (bf16*)a.wT, a.H, a.E,
                                              CTp * 16);
   }
-#define MOE_ROUTE_CASE(ct)                                                                  \
-  case ct:                                                                                  \
-    if ((err = allow_lds(k_route_bf16<ct>, lds)) != hipSuccess) return err;                 \
-    k_route_bf16<ct><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.wT, a.bias,   \
-                                             a.logits, a.topk_ids, a.topk_w, a.hist, a.psum, \
-                                             a.lrank, a.T, a.H, a.E, a.K, nblk);             \
-    break;
   switch (CTp) {
-    MOE_ROUTE_CASE(1)
-    MOE_ROUTE_CASE(2)
-    MOE_ROUTE_CASE(4)
-    MOE_ROUTE_CASE(8)
-    MOE_ROUTE_CASE(16)
-    default:
-      return hipErrorInvalidValue;
+    case 1: return launch_route_bf16<1>(a, nblk, st);
+    case 2: return launch_route_bf16<2>(a, nblk, st);
+    case 4: return launch_route_bf16<4>(a, nblk, st);
+    case 8: return launch_route_bf16<8>(a, nblk, st);
+    case 16: return launch_route_bf16<16>(a, nblk, st);
+    default: return hipErrorInvalidValue;
   }
-#undef MOE_ROUTE_CASE
-  return hipGetLastError();
 }
 
 }  // namespace moe
