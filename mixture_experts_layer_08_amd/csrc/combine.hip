@@ -119,20 +119,21 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
 }
 
 // aux = E * sum_e (count_e / (T K)) (P_e) with P_e = (1/T) sum_t p[t,e].
-// One workgroup of 256 threads.  Expert e's per-block partials are split over
-// G = 256 / E_pad threads (E_pad = E rounded up to a power of two): thread
-// (e, g) sums blocks g, g+G, g+2G, ... in order (fp64), then a fixed-shape
-// tree over g combines them, and thread 0 adds the per-expert terms in
-// expert order.  Deterministic: every sum has a fixed order.
-__global__ __launch_bounds__(256) void k_aux(const int32_t* __restrict__ hist,
-                                             const float* __restrict__ psum,
-                                             float* __restrict__ aux, int T, int E, int K,
-                                             int nblk) {
-  __shared__ double s_p[256];
-  __shared__ long long s_c[256];
+// One workgroup of kAuxThreads threads.  Expert e's per-block partials are
+// split over G = kAuxThreads / E_pad threads (E_pad = E rounded up to a power
+// of two): thread (e, g) sums blocks g, g+G, g+2G, ... in order (fp64), then a
+// fixed-shape tree over g combines them, and thread 0 adds the per-expert
+// terms in expert order.  Deterministic: every sum has a fixed order.
+constexpr int kAuxThreads = 1024;
+__global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__ hist,
+                                                     const float* __restrict__ psum,
+                                                     float* __restrict__ aux, int T, int E, int K,
+                                                     int nblk) {
+  __shared__ double s_p[kAuxThreads];
+  __shared__ long long s_c[kAuxThreads];
   int e_pad = 1;
   while (e_pad < E) e_pad <<= 1;
-  const int G = 256 / e_pad;
+  const int G = kAuxThreads / e_pad;
   const int tid = threadIdx.x;
   const int e = tid / G, g = tid % G;
   double P = 0.0;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void k_aux(const int32_t* __restrict__ hist,
 
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int T, int E, int K,
                       int nblk, hipStream_t st) {
-  k_aux<<<1, 256, 0, st>>>(hist, psum, aux, T, E, K, nblk);
+  k_aux<<<1, kAuxThreads, 0, st>>>(hist, psum, aux, T, E, K, nblk);
   return hipGetLastError();
 }
 

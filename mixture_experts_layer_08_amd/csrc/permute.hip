@@ -47,66 +47,91 @@ __global__ __launch_bounds__(256) void k_scan_blocks(const int32_t* __restrict__
   if (tid == 0) counts[e] = carry;
 }
 
-// One workgroup: kept = min(counts, C), offsets = exclusive scan of kept,
-// n_dropped = sum(counts - kept).  E <= 256.
-__global__ __launch_bounds__(256) void k_offsets(const int32_t* __restrict__ counts,
-                                                 int32_t* __restrict__ kept,
-                                                 int32_t* __restrict__ offsets,
-                                                 int32_t* __restrict__ n_dropped, int E, int C) {
-  __shared__ int s_wave[4];
-  __shared__ int s_drop[4];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c = tid < E ? counts[tid] : 0;
-  const int kp = min(c, C);
-  const int incl = wave_inclusive_scan(kp);
-  const int drop = wave_sum(c - kp);
-  if (lane == 63) s_wave[wave] = incl;
-  if (lane == 0) s_drop[wave] = drop;
-  __syncthreads();
-  int before = 0, total = 0, dsum = 0;
+// Segment offsets from the per-expert counts, computed by every permute wave
+// (E <= 256: lane l holds experts 4l .. 4l+3): kept = min(counts, C),
+// offsets = exclusive scan of kept.  Returns this lane's four offsets and the
+// wave-uniform total; the counts are integers, so every wave gets the same.
+__device__ __forceinline__ void segment_offsets(const int32_t* __restrict__ counts, int E, int C,
+                                                int (&off4)[4], int (&kept4)[4], int& drop4,
+                                                int& total) {
+  const int lane = threadIdx.x & 63;
+  int run = 0;
+  drop4 = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    before += w < wave ? s_wave[w] : 0;
-    total += s_wave[w];
-    dsum += s_drop[w];
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    const int c = e < E ? counts[e] : 0;
+    kept4[i] = min(c, C);
+    drop4 += c - kept4[i];
+    off4[i] = run;  // exclusive within the lane
+    run += kept4[i];
   }
-  if (tid < E) {
-    kept[tid] = kp;
-    offsets[tid] = before + incl - kp;
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    *n_dropped = dsum;
-  }
+  const int incl = wave_inclusive_scan(run);
+  const int before = incl - run;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) off4[i] += before;
+  total = __shfl(incl, 63, kWave);
 }
 
 // One wave per token: its row map entries, then the copy of its row to each
 // kept destination.  The row is read from HBM once (16-byte vectors, VPL per
-// lane per chunk, all loads of a chunk issued before its stores).
+// lane per chunk, all loads of a chunk issued before its stores).  The wave
+// of token 0 also publishes kept, offsets and n_dropped.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_permute(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int K, int C,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int E, int K, int C,
     int nblk) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // wave-uniform; the kernel has no barrier
+  if (t >= T) return;  // wave-uniform; the kernel has no barrier (token 0 always runs)
   const int lane = threadIdx.x & 63;
-  int row = -1;
+  // row-map work first (the counts load independently of ids and lrank, so
+  // two dependent round trips precede the copy); the row loads come after,
+  // since vmcnt waits are in issue order
+  int e = 0, lr = 0;
   if (lane < K) {
-    const int e = ids[(size_t)t * K + lane];
-    const int r = base[(size_t)e * nblk + t / kRouteBlock] + lrank[(size_t)t * K + lane];
-    row = r < C ? offsets[e] + r : -1;
-    row_of[(size_t)t * K + lane] = row;
-    if (row >= 0) token_of[row] = t;
+    e = ids[(size_t)t * K + lane];
+    lr = lrank[(size_t)t * K + lane];
   }
+  int off4[4], kept4[4], drop4, total;
+  segment_offsets(counts, E, C, off4, kept4, drop4, total);
+  if (t == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = 4 * lane + i;
+      if (ee < E) {
+        kept[ee] = kept4[i];
+        offsets[ee] = off4[i];
+      }
+    }
+    const int dropped = wave_sum(drop4);
+    if (lane == 0) {
+      offsets[E] = total;
+      *n_dropped = dropped;
+    }
+  }
+  int row = -1;
+  {
+    // offsets[e] lives in lane e/4, slot e%4 (all lanes take part in the shuffles)
+    const int o0 = __shfl(off4[0], e >> 2, kWave), o1 = __shfl(off4[1], e >> 2, kWave);
+    const int o2 = __shfl(off4[2], e >> 2, kWave), o3 = __shfl(off4[3], e >> 2, kWave);
+    const int oe = (e & 3) == 0 ? o0 : (e & 3) == 1 ? o1 : (e & 3) == 2 ? o2 : o3;
+    if (lane < K) {
+      const int r = base[(size_t)e * nblk + t / kRouteBlock] + lr;
+      row = r < C ? oe + r : -1;
+      row_of[(size_t)t * K + lane] = row;
+      if (row >= 0) token_of[row] = t;
+    }
+  }
+  const u32x4* src = x + (size_t)t * nvec;
+  u32x4 v[VPL];
   int rows[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) rows[k] = __shfl(row, k, kWave);
-  const u32x4* src = x + (size_t)t * nvec;
   for (int c0 = 0; c0 < nvec; c0 += 64 * VPL) {
-    u32x4 v[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int c = c0 + lane + 64 * j;
@@ -129,13 +154,12 @@ __global__ __launch_bounds__(256) void k_permute(
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int nblk = (a.T + kRouteBlock - 1) / kRouteBlock;
   k_scan_blocks<<<a.E, 256, 0, st>>>(a.hist, a.base, a.counts, nblk);
-  k_offsets<<<1, 256, 0, st>>>(a.counts, a.kept, a.offsets, a.n_dropped, a.E, a.C);
   const int elem = a.bf16 ? 2 : 4;
   const int nvec = a.H * elem / 16;
   const int grid = (a.T + 3) / 4;
-  k_permute<8><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.offsets,
-                                     a.row_of, a.token_of, (u32x4*)a.xp, a.T, nvec, a.K, a.C,
-                                     nblk);
+  k_permute<8><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.counts,
+                                     a.kept, a.offsets, a.n_dropped, a.row_of, a.token_of,
+                                     (u32x4*)a.xp, a.T, nvec, a.E, a.K, a.C, nblk);
   return hipGetLastError();
 }
 
