@@ -1,4 +1,4 @@
-"""CPU oracle of the top-k-routed MoE-layer forward (test infrastructure).
+"""CPU oracle of the top-k-routed MoE layer, forward and backward (test infrastructure).
 
 This module is test infrastructure, not product code.  Only the tests, the
 smoke check of ``__graft_entry__`` and the CPU-baseline leg of ``bench.py``
@@ -40,6 +40,19 @@ the design notes of the repository):
   Gimpel's GELU).
 * Optional shared expert: the same FFN applied to every token with weight 1
   ([comm] 2.3, fine-grained plus shared experts).
+
+Backward (the gradient of a scalar L = <dy, y> + alpha * aux, by the chain
+rule of the forward definition above):
+
+* The routing decisions (top-k sets, capacity drops, the counts f_e) are
+  piecewise constant in the logits and get no gradient; the gradient reaches
+  the gate through the renormalised top-k weights ([infra] 3.1: the gate must
+  receive gradients) and through P_e of the aux loss.
+* A dropped assignment contributes nothing to y, so it passes no gradient to
+  the expert FFN or to its routing weight ([comm] 3.2, second pitfall:
+  dropped tokens are absent in the backward pass, their gradient masked).
+* alpha is the aux-loss coefficient of [comm] 3.2 (aux_loss = alpha * N *
+  sum f_i P_i); the forward reports aux without it.
 """
 
 from __future__ import annotations
@@ -327,3 +340,116 @@ def dense_all_experts(x, w1, w2, routing: Dict[str, np.ndarray], ws1=None, ws2=N
     if ws1 is not None:
         y += ffn(x, ws1, ws2)
     return y
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3):
+
+    0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) sqrt(2/pi) (1 + 3 * 0.044715 u^2).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    th = np.tanh(c * (u + 0.044715 * u * u * u))
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * u * u)
+
+
+def ffn_backward(rows, w1, w2, dout):
+    """Gradients of out = GELU(rows W1) W2 for a given d(out).
+
+    Returns (d rows, dW1, dW2), all float64.
+    """
+    a = np.asarray(rows, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    u = a @ w1
+    g = gelu_tanh(u)
+    dg = dout @ w2.T
+    du = dg * gelu_tanh_grad(u)
+    return du @ w1.T, a.T @ du, g.T @ dout
+
+
+def combine_backward(dy, out, row_of, w):
+    """Adjoint of :func:`combine` for the routed part.
+
+    d out[row_of[t,k]] = w[t,k] dy[t] and d w[t,k] = <dy[t], out[row_of[t,k]]>
+    for kept (t, k); a dropped slot gets d w = 0 and touches no row.
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    T, K = row_of.shape
+    dout = np.zeros_like(np.asarray(out, dtype=np.float64))
+    dw = np.zeros((T, K), dtype=np.float64)
+    for k in range(K):
+        r = row_of[:, k]
+        m = r >= 0
+        dout[r[m]] += w[m, k][:, None] * dy[m]
+        dw[m, k] = np.sum(dy[m] * out[r[m]], axis=1)
+    return dout, dw
+
+
+def route_backward(logits, ids, w, dw, E: int, K: int, alpha: float):
+    """d L / d logits from the routing weights and from alpha * aux.
+
+    Weights: w = softmax over the chosen logits ([comm] 3.2 form, equal to
+    [infra] 3.1's p_sel / sum p_sel), so for chosen expert s_k
+    dl[t, s_k] = w_k (dw_k - sum_j w_j dw_j); unchosen experts get nothing
+    from this path.  Aux: P_e = (1/T) sum_t p[t,e] with p the full softmax,
+    f_e fixed, so d aux / d l[t,e] = (E/T) p[t,e] (f_e - sum_e' f_e' p[t,e']).
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    T = l.shape[0]
+    ids64 = ids.astype(np.int64)
+    dl = np.zeros((T, E), dtype=np.float64)
+    s = np.sum(w * dw, axis=1, keepdims=True)
+    np.put_along_axis(dl, ids64, w * (dw - s), axis=1)
+    if alpha != 0.0:
+        p = softmax(l)
+        f = expert_counts(ids, E).astype(np.float64) / float(T * K)
+        dl += alpha * (E / float(T)) * p * (f[None, :] - (p @ f)[:, None])
+    return dl
+
+
+def backward(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, dy, K: int, cf: float,
+             alpha: float = 0.0, logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Every gradient of L = <dy, y> + alpha * aux for one layer forward.
+
+    Routing is that of :func:`forward` with the same arguments (from the given
+    logits when passed).  Returns dx, dw_r, db_r, dw1, dw2, dws1, dws2 and the
+    intermediates d_out (rows of the packed expert outputs), d_w (routing
+    weights), d_xp (rows of the packed inputs) and d_logits.
+    """
+    fw = forward(x, w_r, b_r, w1, w2, ws1, ws2, K=K, cf=cf, logits=logits)
+    E = w1.shape[0]
+    x64 = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    row_of, offsets = fw["row_of"], fw["offsets"]
+    dout, dw = combine_backward(dy, fw["out"], row_of, fw["w"])
+    dxp = np.zeros_like(fw["xp"], dtype=np.float64)
+    dw1 = np.zeros(w1.shape, dtype=np.float64)
+    dw2 = np.zeros(w2.shape, dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            dxp[a:b], dw1[e], dw2[e] = ffn_backward(fw["xp"][a:b], w1[e], w2[e], dout[a:b])
+    # un-permute: each kept row's gradient returns to its token
+    dx = np.zeros_like(x64)
+    for k in range(K):
+        r = row_of[:, k]
+        m = r >= 0
+        dx[m] += dxp[r[m]]
+    l_sel = np.asarray(logits, dtype=np.float64) if logits is not None \
+        else fw["logits_oracle"].astype(np.float32).astype(np.float64)
+    dl = route_backward(l_sel, fw["ids"], fw["w"], dw, E, K, alpha)
+    dx += dl @ np.asarray(w_r, dtype=np.float64).T
+    dw_r = x64.T @ dl
+    db_r = dl.sum(axis=0)
+    dws1 = dws2 = None
+    if ws1 is not None:
+        dxs, dws1, dws2 = ffn_backward(x64, ws1, ws2, dy)
+        dx += dxs
+    return dict(dx=dx, dw_r=dw_r, db_r=db_r, dw1=dw1, dw2=dw2, dws1=dws1, dws2=dws2,
+                d_out=dout, d_w=dw, d_xp=dxp, d_logits=dl, forward=fw)
