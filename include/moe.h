@@ -63,6 +63,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* moe_shape.flags */
 #define MOE_FLAG_LOGITS_IN 1u  /* moe_route reads `logits` instead of running the router GEMM */
+#define MOE_FLAG_TRAIN 2u      /* moe_expert_ffn keeps the GELU pre-activations in the
+                                  workspace for moe_expert_ffn_backward, and the
+                                  workspace also holds the backward's scratch */
 
 typedef struct {
   int32_t T;        /* tokens in the batch                                   */
@@ -92,7 +95,8 @@ int64_t moe_capacity(const moe_shape* s);
  * out need this many rows, hbuf this many rows of h_exp.  -1 if invalid. */
 int64_t moe_max_rows(const moe_shape* s);
 
-/* Bytes of device workspace every call of one forward needs (0 if invalid). */
+/* Bytes of device workspace every call of one forward (and, with
+ * MOE_FLAG_TRAIN, of its backward) needs (0 if invalid). */
 size_t moe_workspace_size(const moe_shape* s);
 
 /*
@@ -170,6 +174,8 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
  *   out      [max_rows,H]     out (dtype); rows >= N untouched
  *   x, ws1 [H,h_shared], ws2 [h_shared,H], hshared [T,h_shared],
  *   shared_out [T,H]          used only when h_shared > 0 (else may be NULL)
+ * With MOE_FLAG_TRAIN the pre-activations xp*W1[e] (and x*Ws1) are also
+ * stored, in dtype, in the workspace for moe_expert_ffn_backward.
  */
 moe_status moe_expert_ffn(const moe_shape* s, const void* xp, const int32_t* offsets,
                           const void* w1, const void* w2, void* hbuf, void* out,
@@ -192,6 +198,105 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* xp, const int32_t* off
 moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_of,
                        const float* topk_w, const void* shared_out, void* y,
                        void* stream);
+
+
+/*
+ * Backward pass.  The gradient of L = <dy, y> + alpha * aux by the chain rule
+ * of the forward above, for a forward run with MOE_FLAG_TRAIN.  The routing
+ * decisions (top-k sets, capacity drops, counts) are held fixed: they are
+ * piecewise constant in the logits.  The gradient reaches the gate through
+ * the renormalised top-k weights ([infra] 3.1: the gate network must receive
+ * gradients) and through P_e of the aux loss (alpha is the coefficient of
+ * [comm] 3.2's aux_loss = alpha * N * sum f_i P_i).  A dropped assignment
+ * passes no gradient ([comm] 3.2, second pitfall: dropped tokens are absent
+ * in the backward pass).  Call order on one stream, one workspace:
+ *   moe_combine_backward, moe_route_backward, moe_expert_ffn_backward,
+ *   moe_permute_backward.
+ * Weight gradients are fp32 and overwritten (not accumulated); activation
+ * gradients are in dtype.  Every result is deterministic.
+ */
+
+/*
+ * moe_combine_backward - adjoint of moe_combine's routed part.
+ *   d_out[row_of[t,k]] = topk_w[t,k] * dy[t]            (dtype)
+ *   d_topk_w[t,k]      = <dy[t], out[row_of[t,k]]>      (fp32, 0 when dropped)
+ *
+ *   dy        [T,H]        gradient of y (dtype)
+ *   out, row_of, topk_w    as given to moe_combine
+ *   d_out     [max_rows,H] out (dtype); rows >= N untouched
+ *   d_topk_w  [T,K]        out (fp32)
+ */
+moe_status moe_combine_backward(const moe_shape* s, const void* dy, const void* out,
+                                const int32_t* row_of, const float* topk_w, void* d_out,
+                                float* d_topk_w, void* stream);
+
+/*
+ * moe_route_backward - gradient of the router.
+ *   d_logits[t, e] = [e chosen as slot k] w_k (d_w_k - sum_j w_j d_w_j)
+ *                    + alpha * (E/T) p[t,e] (f_e - sum_e' f_e' p[t,e'])
+ * with w = topk_w, p the softmax of the logits row and f_e = counts[e]/(T*K);
+ * then d_w_router = x^T d_logits and d_b_router = sum_t d_logits[t] (fp32,
+ * fixed summation order).
+ *
+ *   x [T,H], w_router [H,E]      as given to moe_route (dtype)
+ *   logits, topk_ids, topk_w     from moe_route; counts from moe_permute
+ *   d_topk_w  [T,K]              from moe_combine_backward
+ *   alpha                        aux-loss coefficient (0: no aux term)
+ *   d_logits  [T,E]              out (fp32)
+ *   d_w_router [H,E]             out (fp32)
+ *   d_b_router [E]               out (fp32), or NULL
+ */
+moe_status moe_route_backward(const moe_shape* s, const void* x, const float* logits,
+                              const int32_t* topk_ids, const float* topk_w,
+                              const float* d_topk_w, const int32_t* counts, float alpha,
+                              float* d_logits, float* d_w_router, float* d_b_router,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_backward - gradient of the grouped expert FFN (and of the
+ * shared expert when h_shared > 0), from the pre-activations u = xp*W1[e]
+ * that the MOE_FLAG_TRAIN forward left in the workspace (this call
+ * overwrites them with d u).  For every row r of segment e:
+ *   d_u[r]  = (d_out[r] * W2[e]^T) .* GELU'(u[r])
+ *   d_w2[e] = hbuf_e^T d_out_e,  d_w1[e] = xp_e^T d_u_e   (fp32)
+ *   d_xp[r] = d_u[r] * W1[e]^T                            (dtype)
+ * and for the shared expert the same with x, Ws1, Ws2, hshared and dy:
+ *   d_ws1, d_ws2 (fp32), d_x_shared = d_us * Ws1^T (dtype).
+ *
+ *   xp, offsets, w1, w2, hbuf     as in the forward
+ *   d_out     [max_rows,H]        from moe_combine_backward
+ *   d_xp      [max_rows,H]        out (dtype); rows >= N untouched
+ *   d_w1 [E,H,h_exp], d_w2 [E,h_exp,H]   out (fp32; zero for an empty expert)
+ *   x, ws1, ws2, hshared, dy [T,H], d_x_shared [T,H], d_ws1 [H,h_shared],
+ *   d_ws2 [h_shared,H]            used only when h_shared > 0
+ */
+moe_status moe_expert_ffn_backward(const moe_shape* s, const void* xp, const int32_t* offsets,
+                                   const void* w1, const void* w2, const void* hbuf,
+                                   const void* d_out, void* d_xp, float* d_w1, float* d_w2,
+                                   const void* x, const void* ws1, const void* ws2,
+                                   const void* hshared, const void* dy, void* d_x_shared,
+                                   float* d_ws1, float* d_ws2, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
+ * moe_permute_backward - gradient of x: the adjoint of the dispatch copy
+ * plus the router's and the shared expert's input gradients,
+ *   dx[t] = sum_{k kept} d_xp[row_of[t,k]] (+ d_x_shared[t])
+ *           + d_logits[t] * W_r^T
+ * (the first part summed in fp32 in slot order; in bf16 mode the last term
+ * uses d_logits rounded to bf16).
+ *
+ *   d_xp      [max_rows,H]   from moe_expert_ffn_backward
+ *   row_of    [T,K]
+ *   d_x_shared [T,H] or NULL (required when h_shared > 0)
+ *   d_logits  [T,E]          from moe_route_backward
+ *   w_router  [H,E]          (dtype)
+ *   dx        [T,H]          out (dtype)
+ */
+moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int32_t* row_of,
+                                const void* d_x_shared, const float* d_logits,
+                                const void* w_router, void* dx, void* ws, size_t ws_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

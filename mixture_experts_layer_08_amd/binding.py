@@ -23,12 +23,14 @@ MOE_ERR_HIP = 4
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_LOGITS_IN = 1
+MOE_FLAG_TRAIN = 2
 
 # Every symbol include/moe.h declares.
 EXPORTS = (
     "moe_status_string", "moe_check_shape", "moe_capacity", "moe_max_rows",
     "moe_workspace_size", "moe_route", "moe_aux_loss", "moe_permute",
-    "moe_expert_ffn", "moe_combine",
+    "moe_expert_ffn", "moe_combine", "moe_combine_backward", "moe_route_backward",
+    "moe_expert_ffn_backward", "moe_permute_backward",
 )
 
 
@@ -85,6 +87,15 @@ def lib():
         L.moe_expert_ffn.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P]
+        L.moe_combine_backward.restype = ctypes.c_int
+        L.moe_combine_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_route_backward.restype = ctypes.c_int
+        L.moe_route_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                         _P, _P, _SZ, _P]
+        L.moe_expert_ffn_backward.restype = ctypes.c_int
+        L.moe_expert_ffn_backward.argtypes = [_SHAPE] + [_P] * 18 + [_SZ, _P]
+        L.moe_permute_backward.restype = ctypes.c_int
+        L.moe_permute_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         _lib = L
     return _lib
 
@@ -166,3 +177,32 @@ def moe_combine(s, out, row_of, topk_w, shared_out, y, stream=None):
     _check("moe_combine", lib().moe_combine(
         ctypes.byref(s), _ptr(out), _ptr(row_of), _ptr(topk_w), _ptr(shared_out), _ptr(y),
         _stream(stream)))
+
+
+def moe_combine_backward(s, dy, out, row_of, topk_w, d_out, d_topk_w, stream=None):
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        ctypes.byref(s), _ptr(dy), _ptr(out), _ptr(row_of), _ptr(topk_w), _ptr(d_out),
+        _ptr(d_topk_w), _stream(stream)))
+
+
+def moe_route_backward(s, x, logits, topk_ids, topk_w, d_topk_w, counts, alpha, d_logits,
+                       d_w_router, d_b_router, ws, stream=None):
+    _check("moe_route_backward", lib().moe_route_backward(
+        ctypes.byref(s), _ptr(x), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(d_topk_w),
+        _ptr(counts), float(alpha), _ptr(d_logits), _ptr(d_w_router), _ptr(d_b_router),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_ffn_backward(s, xp, offsets, w1, w2, hbuf, d_out, d_xp, d_w1, d_w2, x, ws1, ws2,
+                            hshared, dy, d_x_shared, d_ws1, d_ws2, ws, stream=None):
+    _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
+        ctypes.byref(s), _ptr(xp), _ptr(offsets), _ptr(w1), _ptr(w2), _ptr(hbuf), _ptr(d_out),
+        _ptr(d_xp), _ptr(d_w1), _ptr(d_w2), _ptr(x), _ptr(ws1), _ptr(ws2), _ptr(hshared),
+        _ptr(dy), _ptr(d_x_shared), _ptr(d_ws1), _ptr(d_ws2), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def moe_permute_backward(s, d_xp, row_of, d_x_shared, d_logits, w_router, dx, ws, stream=None):
+    _check("moe_permute_backward", lib().moe_permute_backward(
+        ctypes.byref(s), _ptr(d_xp), _ptr(row_of), _ptr(d_x_shared), _ptr(d_logits),
+        _ptr(w_router), _ptr(dx), _ptr(ws), _nbytes(ws), _stream(stream)))

@@ -1,6 +1,7 @@
-// C ABI of the MoE-layer forward (declared in include/moe.h): argument
-// validation, workspace layout and kernel launches.  Every check runs on the
-// host before any HIP call, so invalid arguments never reach a kernel.
+// C ABI of the MoE layer, forward and backward (declared in include/moe.h):
+// argument validation, workspace layout and kernel launches.  Every check
+// runs on the host before any HIP call, so invalid arguments never reach a
+// kernel.
 #include <math.h>
 #include <string.h>
 
@@ -17,8 +18,16 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct WsLayout {
-  size_t wT, hist, psum, base, lrank, total;
+  size_t wT, hist, psum, base, lrank;
+  // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
+  // weight gradient's partials, and bf16 copies of d_logits / W_r padded to
+  // a multiple of 8 experts for the d_logits * W_r^T GEMM
+  size_t preact, preact_sh, part, dbpart, dl8, wr8;
+  size_t total;
 };
+
+int64_t max_rows_of(const moe_shape* s);
+int pad8(int v) { return (v + 7) & ~7; }
 
 int n_route_blocks(const moe_shape* s) { return (s->T + kRouteBlock - 1) / kRouteBlock; }
 
@@ -36,6 +45,22 @@ WsLayout ws_layout(const moe_shape* s) {
   off += align_up((size_t)s->E * nblk * 4);
   L.lrank = off;
   off += align_up((size_t)s->T * s->K * 4);
+  if (s->flags & MOE_FLAG_TRAIN) {
+    const size_t elem = s->dtype == MOE_BF16 ? 2 : 4;
+    const size_t nch = (size_t)route_bwd_chunks(s->T);
+    L.preact = off;
+    off += align_up((size_t)max_rows_of(s) * s->h_exp * elem);
+    L.preact_sh = off;
+    off += align_up((size_t)s->T * s->h_shared * elem);
+    L.part = off;
+    off += align_up(nch * s->H * s->E * 4);
+    L.dbpart = off;
+    off += align_up(nch * s->E * 4);
+    L.dl8 = off;
+    if (s->dtype == MOE_BF16) off += align_up((size_t)s->T * pad8(s->E) * 2);
+    L.wr8 = off;
+    if (s->dtype == MOE_BF16) off += align_up((size_t)s->H * pad8(s->E) * 2);
+  }
   L.total = off;
   return L;
 }
@@ -53,6 +78,53 @@ T* at(void* ws, size_t off) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// GEMM over rows (NN / NT): C [rows][N] = A [rows][Kd] * B_g (or B_g^T).
+GemmArgs rows_gemm(int layout, int epi, const void* A, const void* B, void* C, void* E,
+                   const int32_t* offsets, int G, int fixed_rows, int max_rows, int Kd, int N) {
+  GemmArgs g;
+  g.layout = layout;
+  g.epi = epi;
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.E = E;
+  g.offsets = offsets;
+  g.G = G;
+  g.fixed_rows = fixed_rows;
+  g.max_rows = max_rows;
+  g.Kd = Kd;
+  g.N = N;
+  return g;
+}
+
+// Weight-gradient GEMM (TN): C [G][M][N] fp32 = A_g^T [M][rows_g] * B_g [rows_g][N].
+GemmArgs tn_gemm(const void* A, const void* B, float* C, const int32_t* offsets, int G,
+                 int fixed_rows, int M, int N) {
+  GemmArgs g;
+  g.layout = kGemmTN;
+  g.epi = kEpiStore;
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.offsets = offsets;
+  g.G = G;
+  g.fixed_rows = fixed_rows;
+  g.M = M;
+  g.N = N;
+  return g;
+}
+
+}  // namespace
+
+extern "C" int64_t moe_capacity(const moe_shape* s);
+
+namespace {
+int64_t max_rows_of(const moe_shape* s) {
+  const int64_t C = moe_capacity(s);
+  if (C < 0) return -1;
+  const int64_t TK = (int64_t)s->T * s->K, EC = (int64_t)s->E * C;
+  return TK < EC ? TK : EC;
+}
 }  // namespace
 
 extern "C" {
@@ -74,7 +146,7 @@ moe_status moe_check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->K > s->E) return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (s->flags & ~MOE_FLAG_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+  if (s->flags & ~(MOE_FLAG_LOGITS_IN | MOE_FLAG_TRAIN)) return MOE_ERR_INVALID_ARG;
   if (!isfinite(s->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (s->K > 8 || s->E > 256) return MOE_ERR_UNSUPPORTED;
   if (s->H % 8 || s->h_exp % 8 || s->h_shared % 8) return MOE_ERR_UNSUPPORTED;
@@ -95,12 +167,7 @@ int64_t moe_capacity(const moe_shape* s) {
   return (int64_t)c;
 }
 
-int64_t moe_max_rows(const moe_shape* s) {
-  const int64_t C = moe_capacity(s);
-  if (C < 0) return -1;
-  const int64_t TK = (int64_t)s->T * s->K, EC = (int64_t)s->E * C;
-  return TK < EC ? TK : EC;
-}
+int64_t moe_max_rows(const moe_shape* s) { return max_rows_of(s); }
 
 size_t moe_workspace_size(const moe_shape* s) {
   if (moe_check_shape(s) != MOE_OK) return 0;
@@ -208,13 +275,22 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* xp, const int32_t* off
               : launch_grouped_gemm_f32(g, (hipStream_t)stream);
   };
   const int max_rows = (int)moe_max_rows(s);
-  GemmArgs g1{xp, w1, hbuf, offsets, s->E, 0, max_rows, s->H, s->h_exp, 1};
-  GemmArgs g2{hbuf, w2, out, offsets, s->E, 0, max_rows, s->h_exp, s->H, 0};
+  const bool train = (s->flags & MOE_FLAG_TRAIN) != 0;
+  const WsLayout L = ws_layout(s);
+  // GEMM1 (+GELU; with MOE_FLAG_TRAIN the pre-activations are kept), GEMM2
+  const GemmArgs g1 = rows_gemm(kGemmNN, train ? kEpiGeluSave : kEpiGelu, xp, w1, hbuf,
+                                train ? at<void>(ws, L.preact) : nullptr, offsets, s->E, 0,
+                                max_rows, s->H, s->h_exp);
+  const GemmArgs g2 = rows_gemm(kGemmNN, kEpiStore, hbuf, w2, out, nullptr, offsets, s->E, 0,
+                                max_rows, s->h_exp, s->H);
   hipError_t e = gemm(g1);
   if (e == hipSuccess) e = gemm(g2);
   if (e == hipSuccess && shared) {
-    GemmArgs s1{x, ws1, hshared, nullptr, 1, s->T, s->T, s->H, s->h_shared, 1};
-    GemmArgs s2{hshared, ws2, shared_out, nullptr, 1, s->T, s->T, s->h_shared, s->H, 0};
+    const GemmArgs s1 = rows_gemm(kGemmNN, train ? kEpiGeluSave : kEpiGelu, x, ws1, hshared,
+                                  train ? at<void>(ws, L.preact_sh) : nullptr, nullptr, 1, s->T,
+                                  s->T, s->H, s->h_shared);
+    const GemmArgs s2 = rows_gemm(kGemmNN, kEpiStore, hshared, ws2, shared_out, nullptr, nullptr,
+                                  1, s->T, s->T, s->h_shared, s->H);
     e = gemm(s1);
     if (e == hipSuccess) e = gemm(s2);
   }
@@ -240,6 +316,171 @@ moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_o
   a.K = s->K;
   if (s->h_shared > 0 && !shared_out) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(a, (hipStream_t)stream));
+}
+
+
+moe_status moe_combine_backward(const moe_shape* s, const void* dy, const void* out,
+                                const int32_t* row_of, const float* topk_w, void* d_out,
+                                float* d_topk_w, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!dy || !out || !row_of || !topk_w || !d_out || !d_topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(out) || !aligned16(d_out)) return MOE_ERR_INVALID_ARG;
+  CombineBwdArgs a{};
+  a.bf16 = s->dtype == MOE_BF16;
+  a.dy = dy;
+  a.out = out;
+  a.row_of = row_of;
+  a.topk_w = topk_w;
+  a.d_out = d_out;
+  a.d_topk_w = d_topk_w;
+  a.T = s->T;
+  a.H = s->H;
+  a.K = s->K;
+  return hip_status(launch_combine_bwd(a, (hipStream_t)stream));
+}
+
+moe_status moe_route_backward(const moe_shape* s, const void* x, const float* logits,
+                              const int32_t* topk_ids, const float* topk_w,
+                              const float* d_topk_w, const int32_t* counts, float alpha,
+                              float* d_logits, float* d_w_router, float* d_b_router,
+                              void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!(s->flags & MOE_FLAG_TRAIN)) return MOE_ERR_INVALID_ARG;
+  if (!x || !logits || !topk_ids || !topk_w || !d_topk_w || !counts || !d_logits ||
+      !d_w_router)
+    return MOE_ERR_INVALID_ARG;
+  if (!isfinite(alpha)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  RouteBwdArgs a{};
+  a.bf16 = s->dtype == MOE_BF16;
+  a.x = x;
+  a.logits = logits;
+  a.topk_ids = topk_ids;
+  a.topk_w = topk_w;
+  a.d_topk_w = d_topk_w;
+  a.counts = counts;
+  a.alpha = alpha;
+  a.d_logits = d_logits;
+  a.d_w_router = d_w_router;
+  a.d_b_router = d_b_router;
+  a.part = at<float>(ws, L.part);
+  a.dbpart = at<float>(ws, L.dbpart);
+  a.T = s->T;
+  a.H = s->H;
+  a.E = s->E;
+  a.K = s->K;
+  return hip_status(launch_route_bwd(a, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_backward(const moe_shape* s, const void* xp, const int32_t* offsets,
+                                   const void* w1, const void* w2, const void* hbuf,
+                                   const void* d_out, void* d_xp, float* d_w1, float* d_w2,
+                                   const void* x, const void* ws1, const void* ws2,
+                                   const void* hshared, const void* dy, void* d_x_shared,
+                                   float* d_ws1, float* d_ws2, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!(s->flags & MOE_FLAG_TRAIN)) return MOE_ERR_INVALID_ARG;
+  if (!xp || !offsets || !w1 || !w2 || !hbuf || !d_out || !d_xp || !d_w1 || !d_w2)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xp) || !aligned16(w1) || !aligned16(w2) || !aligned16(hbuf) ||
+      !aligned16(d_out) || !aligned16(d_xp) || !aligned16(d_w1) || !aligned16(d_w2))
+    return MOE_ERR_INVALID_ARG;
+  const bool shared = s->h_shared > 0;
+  if (shared) {
+    if (!x || !ws1 || !ws2 || !hshared || !dy || !d_x_shared || !d_ws1 || !d_ws2)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(ws1) || !aligned16(ws2) || !aligned16(hshared) ||
+        !aligned16(dy) || !aligned16(d_x_shared) || !aligned16(d_ws1) || !aligned16(d_ws2))
+      return MOE_ERR_INVALID_ARG;
+  }
+  // A weight-gradient GEMM addresses one expert's whole segment (or all T
+  // rows of the shared expert) through one 32-bit buffer range.
+  const long long elem = s->dtype == MOE_BF16 ? 2 : 4;
+  const long long seg_rows = moe_capacity(s);
+  const long long widest = s->H > s->h_exp ? s->H : s->h_exp;
+  if (seg_rows * widest * elem > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  if (shared && (long long)s->T * (s->H > s->h_shared ? s->H : s->h_shared) * elem > 0x7ffffff0LL)
+    return MOE_ERR_UNSUPPORTED;
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  const bool bf = s->dtype == MOE_BF16;
+  auto gemm = [&](const GemmArgs& g) {
+    return bf ? launch_grouped_gemm_bf16(g, (hipStream_t)stream)
+              : launch_grouped_gemm_f32(g, (hipStream_t)stream);
+  };
+  const int max_rows = (int)moe_max_rows(s);
+  void* u = at<void>(ws, L.preact);  // pre-activations in, d u out (in place)
+  // d u = (d_out W2^T) .* GELU'(u);  d W2 = hbuf^T d_out;  d W1 = xp^T d u;  d xp = d u W1^T
+  hipError_t e = gemm(rows_gemm(kGemmNT, kEpiGeluGrad, d_out, w2, u, u, offsets, s->E, 0,
+                                max_rows, s->H, s->h_exp));
+  if (e == hipSuccess) e = gemm(tn_gemm(hbuf, d_out, d_w2, offsets, s->E, 0, s->h_exp, s->H));
+  if (e == hipSuccess) e = gemm(tn_gemm(xp, u, d_w1, offsets, s->E, 0, s->H, s->h_exp));
+  if (e == hipSuccess)
+    e = gemm(rows_gemm(kGemmNT, kEpiStore, u, w1, d_xp, nullptr, offsets, s->E, 0, max_rows,
+                       s->h_exp, s->H));
+  if (e == hipSuccess && shared) {
+    void* us = at<void>(ws, L.preact_sh);
+    const int T = s->T, hs = s->h_shared;
+    e = gemm(rows_gemm(kGemmNT, kEpiGeluGrad, dy, ws2, us, us, nullptr, 1, T, T, s->H, hs));
+    if (e == hipSuccess) e = gemm(tn_gemm(hshared, dy, d_ws2, nullptr, 1, T, hs, s->H));
+    if (e == hipSuccess) e = gemm(tn_gemm(x, us, d_ws1, nullptr, 1, T, s->H, hs));
+    if (e == hipSuccess)
+      e = gemm(rows_gemm(kGemmNT, kEpiStore, us, ws1, d_x_shared, nullptr, nullptr, 1, T, T, hs,
+                         s->H));
+  }
+  return hip_status(e);
+}
+
+moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int32_t* row_of,
+                                const void* d_x_shared, const float* d_logits,
+                                const void* w_router, void* dx, void* ws, size_t ws_bytes,
+                                void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!(s->flags & MOE_FLAG_TRAIN)) return MOE_ERR_INVALID_ARG;
+  if (!d_xp || !row_of || !d_logits || !w_router || !dx) return MOE_ERR_INVALID_ARG;
+  if (s->h_shared > 0 && !d_x_shared) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(d_xp) || !aligned16(dx) || (d_x_shared && !aligned16(d_x_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  const bool bf = s->dtype == MOE_BF16;
+  hipStream_t hs = (hipStream_t)stream;
+  PermuteBwdArgs a{};
+  a.bf16 = bf;
+  a.d_xp = d_xp;
+  a.row_of = row_of;
+  a.d_x_shared = s->h_shared > 0 ? d_x_shared : nullptr;
+  a.dx = dx;
+  a.T = s->T;
+  a.H = s->H;
+  a.K = s->K;
+  hipError_t e = launch_permute_bwd(a, hs);
+  // dx += d_logits W_r^T: an NT GEMM with K = E accumulating into dx; in bf16
+  // mode over copies padded to a multiple of 8 experts (16-byte rows)
+  if (e == hipSuccess) {
+    if (bf) {
+      const int E8 = pad8(s->E);
+      bf16* dl8 = at<bf16>(ws, L.dl8);
+      bf16* wr8 = at<bf16>(ws, L.wr8);
+      e = launch_pad_bf16(d_logits, true, dl8, s->T, s->E, E8, hs);
+      if (e == hipSuccess) e = launch_pad_bf16(w_router, false, wr8, s->H, s->E, E8, hs);
+      if (e == hipSuccess)
+        e = launch_grouped_gemm_bf16(rows_gemm(kGemmNT, kEpiAccum, dl8, wr8, dx, nullptr,
+                                               nullptr, 1, s->T, s->T, E8, s->H),
+                                     hs);
+    } else {
+      e = launch_grouped_gemm_f32(rows_gemm(kGemmNT, kEpiAccum, d_logits, w_router, dx, nullptr,
+                                            nullptr, 1, s->T, s->T, s->E, s->H),
+                                  hs);
+    }
+  }
+  return hip_status(e);
 }
 
 }  // extern "C"

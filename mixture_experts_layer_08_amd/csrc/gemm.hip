@@ -1,6 +1,9 @@
-// Grouped GEMM over variable-length expert segments:
+// Grouped GEMM over variable-length expert segments.  Forward form (NN):
 //   C[r, :] = act(A[r, :] * B[g])   for every row r of segment g,
 // with segment g the rows [offsets[g], offsets[g+1]) of the packed buffer.
+// The backward pass adds NT (A[r, :] * B[g]^T, the transposed weights) and
+// TN (C[g] = A_g^T B_g over the rows of segment g: per-expert weight
+// gradients); see GemmLayout.
 //
 // Method: the per-expert contractions of the MoELayer listing of the
 // dpshk.com "MoE module infra notes" (section 4.2: x W1 -> GELU -> W2 over
@@ -170,22 +173,65 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
 }
 #pragma clang diagnostic pop
 
+// GELU'(u) of the tanh form: with s = 1 / (1 + exp(-2z)) = 0.5 (1 + tanh z)
+// and 1 - tanh^2 z = 4 s (1 - s):  s + 2 u s (1 - s) z'(u),
+// z'(u) = sqrt(2/pi) (1 + 3 * 0.044715 u^2).
+__device__ __forceinline__ float gelu_tanh_grad_f32(float u) {
+  const float kC = 0.7978845608028654f;           // sqrt(2/pi)
+  const float kNeg2Log2e = -2.8853900817779268f;   // -2 / ln 2
+  const float z = kC * fmaf(0.044715f * u, u * u, u);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNeg2Log2e * z));
+  const float dz = kC * fmaf(3.0f * 0.044715f * u, u, 1.0f);
+  return fmaf(2.0f * u * s * (1.0f - s), dz, s);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Operand staging.  Each operand of a K-step lands in its 16 KiB half of
+// the stage in one of two forms:
+//   K-contiguous rows ("rows": A of NN/NT, B of NT): [256 rows][32 k], 64-byte
+//     rows, 16-byte chunk c at c ^ ((row >> 2) & 3); fragments by ds_read_b128;
+//   row-contiguous k-rows ("cols": B of NN/TN, A of TN): [32 k][256], 512-byte
+//     rows, chunk c at c ^ (4 * (k & 3)); fragments by ds_read_b64_tr_b16 pairs.
+// A fragment is 8 consecutive k of one row/column per lane (row lane % 32,
+// k half lane / 32) whichever form it came from.  Cv and Ep may be the same
+// buffer (the GELU-derivative epilogue in place): each element is read, then
+// written, by one lane.
+template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
-    const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C,
-    const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows, int mt_bound,
-    int Kd, int N, int gelu) {
+    const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv,
+    bf16* Ep, const int32_t* __restrict__ offsets, int G, int fixed_rows,
+    int a_rows, int mt_bound, int M, int Kd, int N) {
+  constexpr bool kTN = LAYOUT == kGemmTN;
+  constexpr bool kARows = !kTN;               // A in "rows" form
+  constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
-  if ((int)blockIdx.x >= mt_bound * nt_count) return;
-  int mt, nt;
-  decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
-  int seg, row0, rows;
-  if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
-  // The lookup result is wave-uniform; keep it in scalar registers so the
-  // buffer descriptors below are scalar too.
+  int mt, nt, seg, row0, rows;
+  int k_begin = 0, k_end = Kd;  // contraction range; TN: the segment's packed rows
+  if (kTN) {
+    const int mt_count = (M + BM2 - 1) / BM2;
+    const int per_seg = mt_count * nt_count;
+    if ((int)blockIdx.x >= G * per_seg) return;
+    seg = blockIdx.x / per_seg;
+    decode_tile(blockIdx.x - seg * per_seg, mt_count, nt_count, mt, nt);
+    k_begin = offsets ? offsets[seg] : 0;
+    k_end = offsets ? offsets[seg + 1] : fixed_rows;
+    row0 = mt * BM2;  // rows of C = columns of A
+    rows = min(BM2, M - row0);
+  } else {
+    if ((int)blockIdx.x >= mt_bound * nt_count) return;
+    decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
+    if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  }
+  // The tile is wave-uniform; keep it in scalar registers so the buffer
+  // descriptors below are scalar too.
   seg = __builtin_amdgcn_readfirstlane(seg);
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
+  k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+  k_end = __builtin_amdgcn_readfirstlane(k_end);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -195,54 +241,102 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- global -> LDS loaders (2 + 2 instructions per wave per stage) ----
-  // A: instruction d of this wave covers stage rows 16*(8d + wave) .. +15,
-  // four lanes per 64-byte row.  Rows [row0, a_rows) are addressable; rows
-  // past the segment are read but their outputs never stored.
-  const u32x4 ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
-  const int a_row_l = lane >> 2;
-  const int a_chunk = a_swz(a_row_l, lane & 3);  // (row >> 2) & 3 is d- and wave-invariant
-  const uint32_t a_off = (uint32_t)((a_row_l + 16 * wave) * Kd + a_chunk * 8) * 2;
-  const uint32_t a_dstride = (uint32_t)(8 * 16 * Kd) * 2;
-  // B: this expert's slice from column n0 on; instruction d of this wave
-  // covers k rows 2*(8d + wave) .. +1, 32 lanes per 512-byte row.  k rows
-  // past Kd lie beyond num_records and read as zero.
-  const u32x4 rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
-  const int b_row0 = (lane >> 5) + 2 * wave;               // (row & 3) is d-invariant
-  const int b_chunk = (lane & 31) ^ (4 * (b_row0 & 3));
-  const uint32_t b_off = (uint32_t)(b_row0 * N + b_chunk * 8) * 2;
-  const uint32_t b_dstride = (uint32_t)(16 * N) * 2;
+  // "rows" form: instruction d of this wave covers stage rows 16*(8d + wave)
+  // .. +15, four lanes per 64-byte row; a k chunk past Kd reads as zero.
+  const int r_row_l = lane >> 2;
+  const int r_chunk = a_swz(r_row_l, lane & 3);  // (row >> 2) & 3 is d- and wave-invariant
+  // "cols" form: instruction d covers k rows 2*(8d + wave) .. +1, 32 lanes per
+  // 512-byte row; k rows past the contraction range lie beyond num_records.
+  const int c_row0 = (lane >> 5) + 2 * wave;     // (row & 3) is d-invariant
+  const int c_chunk = (lane & 31) ^ (4 * (c_row0 & 3));
+  // A
+  u32x4 ra_src;
+  uint32_t a_off, a_dstride, a_kstride;
+  if (kARows) {
+    // rows [row0, a_rows) of A are addressable; rows past the segment are
+    // read but their outputs never stored
+    ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
+    a_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 8) * 2;
+    a_dstride = (uint32_t)(8 * 16 * Kd) * 2;
+    a_kstride = BK2 * 2;
+  } else {
+    // TN: A_g^T; k rows are the segment's packed rows, columns row0.. of A
+    ra_src = make_rsrc_words(A + (size_t)k_begin * M + row0,
+                             ((long long)(k_end - k_begin) * M - row0) * 2);
+    a_off = (uint32_t)(c_row0 * M + c_chunk * 8) * 2;
+    a_dstride = (uint32_t)(16 * M) * 2;
+    a_kstride = (uint32_t)(BK2 * M) * 2;
+  }
+  // B
+  u32x4 rb_src;
+  uint32_t b_off, b_dstride, b_kstride;
+  if (kBRows) {
+    // NT: B_g^T rows n0.. (rows past N lie beyond num_records)
+    rb_src = make_rsrc_words(B + ((size_t)seg * N + n0) * Kd, (long long)(N - n0) * Kd * 2);
+    b_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 8) * 2;
+    b_dstride = (uint32_t)(8 * 16 * Kd) * 2;
+    b_kstride = BK2 * 2;
+  } else if (kTN) {
+    rb_src = make_rsrc_words(B + (size_t)k_begin * N + n0,
+                             ((long long)(k_end - k_begin) * N - n0) * 2);
+    b_off = (uint32_t)(c_row0 * N + c_chunk * 8) * 2;
+    b_dstride = (uint32_t)(16 * N) * 2;
+    b_kstride = (uint32_t)(BK2 * N) * 2;
+  } else {
+    // NN: this expert's slice from column n0 on
+    rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
+    b_off = (uint32_t)(c_row0 * N + c_chunk * 8) * 2;
+    b_dstride = (uint32_t)(16 * N) * 2;
+    b_kstride = (uint32_t)(BK2 * N) * 2;
+  }
 
   // load d (0, 1: A; 2, 3: B) of step kt into the stage at LDS address st
   auto dma = [&](uint32_t st, int d, int kt) {
     const int k0 = kt * BK2;
-    if (d < kDma)
+    if (d < kDma) {
+      const uint32_t off = a_off + d * a_dstride + (uint32_t)kt * a_kstride;
       dma_load16(st + (8 * d + wave) * 1024,
-                 k0 + a_chunk * 8 < Kd ? a_off + d * a_dstride + (uint32_t)k0 * 2 : kOob, ra_src);
-    else
+                 kARows ? (k0 + r_chunk * 8 < Kd ? off : kOob) : off, ra_src);
+    } else {
+      const uint32_t off = b_off + (d - kDma) * b_dstride + (uint32_t)kt * b_kstride;
       dma_load16(st + BM2 * BK2 * 2 + (8 * (d - kDma) + wave) * 1024,
-                 b_off + (d - kDma) * b_dstride + (uint32_t)k0 * N * 2, rb_src);
+                 kBRows ? (k0 + r_chunk * 8 < Kd ? off : kOob) : off, rb_src);
+    }
   };
   auto stage_addr = [&](int kt) {
     return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt % kStages) * kStageBytes);
   };
 
   // ---- LDS -> register operand addresses (relative to a stage) ----
-  // A fragment i, substep ks: row wm*128 + i*32 + rr, chunk 2ks + kh.
-  uint32_t a_rd[kSub];
-#pragma unroll
-  for (int ks = 0; ks < kSub; ++ks)
-    a_rd[ks] = (uint32_t)(wm * 128 + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
-  // B^T fragment j: lane group g = lane/16, i = lane%16 reads k row
-  // (g>>1)*8 + i/4 (+4 for the high half, +16 per substep) at n =
-  // wn*64 + j*32 + (g&1)*16 + 4*(i%4).
+  // "rows" fragment of row r, substep ks: row r, chunk 2ks + kh (b128).
+  // "cols" fragment of column c: lane group g = lane/16, i = lane%16 reads k
+  // row (g>>1)*8 + i/4 (+4 for the high half, +16 per substep) at column
+  // c + (g&1)*16 + 4*(i%4) of its 32-column block.
   const int bg = lane >> 4, bi = lane & 15;
-  const int b_krow = (bg >> 1) * 8 + (bi >> 2);
-  uint32_t b_rd[2];
+  const int c_krow = (bg >> 1) * 8 + (bi >> 2);
+  auto cols_addr = [&](int col) {
+    const int c = col + (bg & 1) * 16 + 4 * (bi & 3);
+    const int chunk = (c >> 3) ^ (4 * (c_krow & 3));
+    return (uint32_t)c_krow * 512 + (uint32_t)chunk * 16 + (uint32_t)(c & 7) * 2;
+  };
+  uint32_t a_rd[4];  // rows form: [ks] (2 used); cols form: [i]
+  if (kARows) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = wn * 64 + j * 32 + (bg & 1) * 16 + 4 * (bi & 3);
-    const int chunk = (n >> 3) ^ (4 * (b_krow & 3));
-    b_rd[j] = BM2 * BK2 * 2 + (uint32_t)b_krow * 512 + (uint32_t)chunk * 16 + (uint32_t)(n & 7) * 2;
+    for (int ks = 0; ks < kSub; ++ks)
+      a_rd[ks] = (uint32_t)(wm * 128 + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_rd[i] = cols_addr(wm * 128 + i * 32);
+  }
+  uint32_t b_rd[2];
+  if (kBRows) {
+#pragma unroll
+    for (int ks = 0; ks < kSub; ++ks)
+      b_rd[ks] = BM2 * BK2 * 2 + (uint32_t)(wn * 64 + rr) * (BK2 * 2) +
+                 (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b_rd[j] = BM2 * BK2 * 2 + cols_addr(wn * 64 + j * 32);
   }
 
   f32x16 acc[4][2];
@@ -253,15 +347,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Operand fragments of one k-substep (16 k): 4 A (b128) + 2 B^T (2 x tr).
+  // Operand fragments of one k-substep (16 k): 4 of A, 2 of B.
   auto read_ops = [&](uint32_t st, int ks, bf16x8* a, bf16x8* b) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = lds_read_b128(st + a_rd[ks] + i * 32 * BK2 * 2);
+    for (int i = 0; i < 4; ++i)
+      a[i] = kARows ? lds_read_b128(st + a_rd[ks] + i * 32 * BK2 * 2)
+                    : lds_read_tr_pair(st + a_rd[i] + ks * 8192, st + a_rd[i] + ks * 8192 + 2048);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      b[j] = lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+      b[j] = kBRows ? lds_read_b128(st + b_rd[ks] + j * 32 * BK2 * 2)
+                    : lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
   };
-  // 8 LDS reads spread between 8 MFMAs (mask 0x008 MFMA, 0x100 DS read).
+  // 8 LDS reads (12 with A in cols form) spread between 8 MFMAs (mask 0x008
+  // MFMA, 0x100 DS read).
   auto mma_reads = [&](const bf16x8* a, const bf16x8* b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -271,7 +369,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kARows ? 1 : (kBRows ? 1 : 2), 0);
     }
   };
   // The last substep's MFMAs with the refill loads of step kt_fill between
@@ -296,7 +394,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // iteration's barrier.  At the wait of iteration kt this wave has issued
   // steps up to kt+kStages-2, so allowing kStages-3 steps in flight means
   // step kt+1 has landed; after the barrier it has landed for every wave.
-  const int KT = (Kd + BK2 - 1) / BK2;
+  const int KT = (k_end - k_begin + BK2 - 1) / BK2;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
     const uint32_t st = stage_addr(s);
@@ -326,7 +424,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   for (int i = 0; i < 4; ++i) {
     const int m = wm * 128 + i * 32 + rr;
     if (m >= rows) continue;
-    bf16* crow = C + (size_t)(row0 + m) * N;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -335,43 +432,92 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
         if (n < N) {
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (gelu) {
+          if (kTN) {
+            float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
+            *(f32x4*)(crow + n) = f32x4{v0, v1, v2, v3};
+            continue;
+          }
+          const size_t at = (size_t)(row0 + m) * N + n;
+          bf16* crow = (bf16*)Cv;
+          if (EPI == kEpiGeluSave)
+            *(u32x2*)(Ep + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          if (EPI == kEpiGelu || EPI == kEpiGeluSave) {
             v0 = gelu_tanh_f32(v0);
             v1 = gelu_tanh_f32(v1);
             v2 = gelu_tanh_f32(v2);
             v3 = gelu_tanh_f32(v3);
+          } else if (EPI == kEpiGeluGrad) {
+            const u32x2 u = *(const u32x2*)(Ep + at);
+            v0 *= gelu_tanh_grad_f32(bf16_lo(u[0]));
+            v1 *= gelu_tanh_grad_f32(bf16_hi(u[0]));
+            v2 *= gelu_tanh_grad_f32(bf16_lo(u[1]));
+            v3 *= gelu_tanh_grad_f32(bf16_hi(u[1]));
+          } else if (EPI == kEpiAccum) {
+            const u32x2 c = *(const u32x2*)(crow + at);
+            v0 += bf16_lo(c[0]);
+            v1 += bf16_hi(c[0]);
+            v2 += bf16_lo(c[1]);
+            v3 += bf16_hi(c[1]);
           }
-          *(u32x2*)(crow + n) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *(u32x2*)(crow + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
       }
     }
   }
 }
 
-// fp32 grouped GEMM (plain FMA, 64 x 64 tiles, 4 x 4 outputs per thread).
+// fp32 grouped GEMM (plain FMA, 64 x 64 tiles, 4 x 4 outputs per thread), in
+// the same layouts and epilogues; operands are gathered with strided loads.
+// C and Ep may be the same buffer (the GELU-derivative epilogue in place):
+// each element is read, then written, by one thread.
+template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(256) void k_grouped_gemm_f32(
-    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C,
-    const int32_t* __restrict__ offsets, int G, int fixed_rows, int mt_bound, int Kd, int N,
-    int gelu) {
+    const float* __restrict__ A, const float* __restrict__ B, float* C,
+    float* Ep, const int32_t* __restrict__ offsets, int G, int fixed_rows,
+    int mt_bound, int M, int Kd, int N) {
   constexpr int TM = 64, TN = 64, TK = 16;
+  constexpr bool kTN = LAYOUT == kGemmTN;
   __shared__ float sA[TM][TK + 1];
   __shared__ float sB[TK][TN];
   const int nt_count = (N + TN - 1) / TN;
-  const int mt = blockIdx.x / nt_count, nt = blockIdx.x % nt_count;
-  int seg, row0, rows;
-  if (!find_segment<TM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
-  const float* Bg = B + (size_t)seg * Kd * N;
+  int mt, nt, seg, row0, rows, k_begin = 0, k_end = Kd;
+  if (kTN) {
+    const int mt_count = (M + TM - 1) / TM;
+    const int per_seg = mt_count * nt_count;
+    seg = blockIdx.x / per_seg;
+    const int t = blockIdx.x - seg * per_seg;
+    mt = t / nt_count;
+    nt = t % nt_count;
+    k_begin = offsets ? offsets[seg] : 0;
+    k_end = offsets ? offsets[seg + 1] : fixed_rows;
+    row0 = mt * TM;
+    rows = min(TM, M - row0);
+  } else {
+    mt = blockIdx.x / nt_count;
+    nt = blockIdx.x % nt_count;
+    if (!find_segment<TM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  }
   const int n0 = nt * TN;
+  const int klen = k_end - k_begin;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kd; k0 += TK) {
+  for (int k0 = 0; k0 < klen; k0 += TK) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = tid + 256 * j;
-      const int r = idx >> 4, c = idx & 15;
-      sA[r][c] = (r < rows && k0 + c < Kd) ? A[(size_t)(row0 + r) * Kd + k0 + c] : 0.0f;
-      const int kr = idx >> 6, nc = idx & 63;
-      sB[kr][nc] = (k0 + kr < Kd && n0 + nc < N) ? Bg[(size_t)(k0 + kr) * N + n0 + nc] : 0.0f;
+      const int r = idx >> 4, c = idx & 15;  // A element (row0 + r, k0 + c)
+      float av = 0.0f;
+      if (r < rows && k0 + c < klen)
+        av = kTN ? A[(size_t)(k_begin + k0 + c) * M + row0 + r] : A[(size_t)(row0 + r) * Kd + k0 + c];
+      sA[r][c] = av;
+      const int kr = idx >> 6, nc = idx & 63;  // B element (k0 + kr, n0 + nc)
+      float bv = 0.0f;
+      if (k0 + kr < klen && n0 + nc < N) {
+        if (LAYOUT == kGemmNN) bv = B[((size_t)seg * Kd + k0 + kr) * N + n0 + nc];
+        else if (LAYOUT == kGemmNT) bv = B[((size_t)seg * N + n0 + nc) * Kd + k0 + kr];
+        else bv = B[(size_t)(k_begin + k0 + kr) * N + n0 + nc];
+      }
+      sB[kr][nc] = bv;
     }
     __syncthreads();
 #pragma unroll
@@ -395,11 +541,18 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = n0 + tx * 4 + j;
-      if (c < N) {
-        float v = acc[i][j];
-        if (gelu) v = gelu_tanh_f32(v);
-        C[(size_t)(row0 + r) * N + c] = v;
+      if (c >= N) continue;
+      float v = acc[i][j];
+      if (kTN) {
+        C[((size_t)seg * M + row0 + r) * N + c] = v;
+        continue;
       }
+      const size_t at = (size_t)(row0 + r) * N + c;
+      if (EPI == kEpiGeluSave) Ep[at] = v;
+      if (EPI == kEpiGelu || EPI == kEpiGeluSave) v = gelu_tanh_f32(v);
+      else if (EPI == kEpiGeluGrad) v *= gelu_tanh_grad_f32(Ep[at]);
+      else if (EPI == kEpiAccum) v += C[at];
+      C[at] = v;
     }
   }
 }
@@ -409,36 +562,72 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
   return (a.max_rows + tm - 1) / tm + a.G;
 }
 
-hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+template <int LAYOUT, int EPI>
+static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
   static bool lds_ok = false;
   if (!lds_ok) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_bf16,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_bf16<LAYOUT, EPI>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)kSmem2);
     if (e != hipSuccess) return e;
     lds_ok = true;
   }
-  const int mtb = mt_bound_for(a, BM2);
   const int ntc = (a.N + BN2 - 1) / BN2;
-  const long long grid = (long long)mtb * ntc;
+  int mtb = 0;
+  long long grid;
+  if (LAYOUT == kGemmTN) {
+    grid = (long long)a.G * ((a.M + BM2 - 1) / BM2) * ntc;
+  } else {
+    mtb = mt_bound_for(a, BM2);
+    grid = (long long)mtb * ntc;
+  }
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_grouped_gemm_bf16<<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
-      (const bf16*)a.A, (const bf16*)a.B, (bf16*)a.C, a.offsets, a.G, a.fixed_rows,
-      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.Kd, a.N, a.gelu);
+  k_grouped_gemm_bf16<LAYOUT, EPI><<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
+      (const bf16*)a.A, (const bf16*)a.B, a.C, (bf16*)a.E, a.offsets, a.G, a.fixed_rows,
+      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm_f32(const GemmArgs& a, hipStream_t st) {
-  const int mtb = mt_bound_for(a, 64);
+template <int LAYOUT, int EPI>
+static hipError_t launch_f32(const GemmArgs& a, hipStream_t st) {
   const int ntc = (a.N + 63) / 64;
-  const long long grid = (long long)mtb * ntc;
+  int mtb = 0;
+  long long grid;
+  if (LAYOUT == kGemmTN) {
+    grid = (long long)a.G * ((a.M + 63) / 64) * ntc;
+  } else {
+    mtb = mt_bound_for(a, 64);
+    grid = (long long)mtb * ntc;
+  }
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_grouped_gemm_f32<<<(unsigned)grid, 256, 0, st>>>((const float*)a.A, (const float*)a.B,
-                                                     (float*)a.C, a.offsets, a.G, a.fixed_rows,
-                                                     mtb, a.Kd, a.N, a.gelu);
+  k_grouped_gemm_f32<LAYOUT, EPI><<<(unsigned)grid, 256, 0, st>>>(
+      (const float*)a.A, (const float*)a.B, (float*)a.C, (float*)a.E, a.offsets, a.G,
+      a.fixed_rows, mtb, a.M, a.Kd, a.N);
   return hipGetLastError();
 }
+
+// The (layout, epilogue) pairs the layer uses.
+#define MOE_GEMM_DISPATCH(LAUNCH)                                               \
+  switch (a.layout * 8 + a.epi) {                                               \
+    case kGemmNN * 8 + kEpiStore: return LAUNCH<kGemmNN, kEpiStore>(a, st);     \
+    case kGemmNN * 8 + kEpiGelu: return LAUNCH<kGemmNN, kEpiGelu>(a, st);       \
+    case kGemmNN * 8 + kEpiGeluSave: return LAUNCH<kGemmNN, kEpiGeluSave>(a, st); \
+    case kGemmNT * 8 + kEpiStore: return LAUNCH<kGemmNT, kEpiStore>(a, st);     \
+    case kGemmNT * 8 + kEpiGeluGrad: return LAUNCH<kGemmNT, kEpiGeluGrad>(a, st); \
+    case kGemmNT * 8 + kEpiAccum: return LAUNCH<kGemmNT, kEpiAccum>(a, st);     \
+    case kGemmTN * 8 + kEpiStore: return LAUNCH<kGemmTN, kEpiStore>(a, st);     \
+    default: return hipErrorInvalidValue;                                       \
+  }
+
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st) {
+  MOE_GEMM_DISPATCH(launch_bf16)
+}
+
+hipError_t launch_grouped_gemm_f32(const GemmArgs& a, hipStream_t st) {
+  MOE_GEMM_DISPATCH(launch_f32)
+}
+#undef MOE_GEMM_DISPATCH
 
 }  // namespace moe

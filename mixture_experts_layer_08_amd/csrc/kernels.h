@@ -8,6 +8,8 @@
 
 #include <algorithm>
 
+#include "common.h"
+
 namespace moe {
 
 // Tokens per route block: the unit of the router's workgroups and of the
@@ -53,16 +55,31 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
+// Operand layouts of the grouped GEMM (the contraction runs over K):
+//   kGemmNN: A [rows][Kd], B [G][Kd][N] -> C [rows][N]; rows segmented by offsets
+//   kGemmNT: A [rows][Kd], B [G][N][Kd] -> C [rows][N]; rows segmented by offsets
+//   kGemmTN: A [rows][M],  B [rows][N]  -> C [G][M][N] (fp32); K = the rows of
+//            segment g, so C[g] = A_g^T B_g (a per-expert weight gradient)
+enum GemmLayout { kGemmNN = 0, kGemmNT = 1, kGemmTN = 2 };
+// Epilogues of NN / NT (TN always stores the fp32 accumulators):
+//   kEpiStore C = acc;  kEpiGelu C = GELU(acc);  kEpiGeluSave C = GELU(acc), E = acc;
+//   kEpiGeluGrad C = acc * GELU'(E);  kEpiAccum C = C + acc.
+enum GemmEpi { kEpiStore = 0, kEpiGelu = 1, kEpiGeluSave = 2, kEpiGeluGrad = 3, kEpiAccum = 4 };
+
 struct GemmArgs {
-  const void* A;        // [rows][Kd]
-  const void* B;        // [G][Kd][N]
-  void* C;              // [rows][N]
-  const int32_t* offsets;  // [G+1] device, or nullptr: one group of fixed_rows rows
-  int G;
-  int fixed_rows;
-  int max_rows;         // upper bound on offsets[G] (sizes the grid)
-  int Kd, N;
-  int gelu;             // 1: C = GELU_tanh(A B), 0: C = A B
+  int layout = kGemmNN;
+  int epi = kEpiStore;
+  const void* A = nullptr;
+  const void* B = nullptr;
+  void* C = nullptr;
+  void* E = nullptr;               // epilogue tensor [rows][N] (written or read, see GemmEpi)
+  const int32_t* offsets = nullptr;  // [G+1] device, or nullptr: one segment of fixed_rows rows
+  int G = 1;
+  int fixed_rows = 0;
+  int max_rows = 0;                // upper bound on offsets[G] (sizes the NN / NT grid)
+  int M = 0;                       // TN: rows of each C block (columns of A)
+  int Kd = 0;                      // NN / NT: contraction length
+  int N = 0;                       // columns of B and C
 };
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& a, hipStream_t st);
@@ -80,5 +97,55 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int T, int E, int K,
                       int nblk, hipStream_t st);
+
+// ---- backward ----
+struct CombineBwdArgs {
+  bool bf16;
+  const void* dy;
+  const void* out;
+  const int32_t* row_of;
+  const float* topk_w;
+  void* d_out;
+  float* d_topk_w;
+  int T, H, K;
+};
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st);
+
+// Tokens per chunk of the router weight gradient's first pass; its partials
+// are [chunks][H][E] fp32.
+constexpr int kRouteBwdChunk = 1024;
+inline int route_bwd_chunks(int T) { return (T + kRouteBwdChunk - 1) / kRouteBwdChunk; }
+
+struct RouteBwdArgs {
+  bool bf16;
+  const void* x;
+  const float* logits;
+  const int32_t* topk_ids;
+  const float* topk_w;
+  const float* d_topk_w;
+  const int32_t* counts;
+  float alpha;
+  float* d_logits;
+  float* d_w_router;
+  float* d_b_router;   // nullable
+  float* part;         // [chunks][H][E] scratch
+  float* dbpart;       // [chunks][E] scratch
+  int T, H, E, K;
+};
+hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
+
+struct PermuteBwdArgs {
+  bool bf16;
+  const void* d_xp;
+  const int32_t* row_of;
+  const void* d_x_shared;  // nullable
+  void* dx;
+  int T, H, K;
+};
+hipError_t launch_permute_bwd(const PermuteBwdArgs& a, hipStream_t st);
+
+// dst [R][Ep] bf16 = src [R][E] (fp32 or bf16), zero-padded to Ep columns.
+hipError_t launch_pad_bf16(const void* src, bool src_f32, bf16* dst, int R, int E, int Ep,
+                           hipStream_t st);
 
 }  // namespace moe

@@ -112,6 +112,16 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
     return dict(x=x, w_r=w_r, b_r=b_r, w1=w1, w2=w2, ws1=ws1, ws2=ws2)
 
 
+def make_grad_output(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """The upstream gradient dy [T,H] of a backward test: N(0,1) drawn from its
+    own generator seeded with ``seed + 7919`` (independent of the forward
+    inputs), rounded to the workload dtype."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 7919)
+    return _randn(gen, (w.T, w.H), 1.0, w.torch_dtype(), device)
+
+
 def to_numpy_f64(t: Optional[torch.Tensor]):
     """Widen a tensor exactly to a float64 numpy array (bf16 and fp32 both fit)."""
     if t is None:

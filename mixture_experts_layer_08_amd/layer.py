@@ -1,8 +1,10 @@
-"""One MoE-layer forward through the C ABI, with torch supplying device memory.
+"""One MoE-layer forward (and backward) through the C ABI, with torch
+supplying device memory.
 
 :class:`MoeBuffers` allocates every output and scratch buffer of a shape once
 (callers reuse it across steps); :func:`forward` issues the five library calls
-in order on one stream.  No arithmetic of the layer happens here.
+in order on one stream, :func:`backward` the four backward calls after a
+forward run with ``train=True``.  No arithmetic of the layer happens here.
 """
 
 from __future__ import annotations
@@ -16,10 +18,10 @@ from . import binding as B
 from .inputs import Workload
 
 
-def shape_of(w: Workload, logits_in: bool = False) -> B.moe_shape:
+def shape_of(w: Workload, logits_in: bool = False, train: bool = False) -> B.moe_shape:
+    flags = (B.MOE_FLAG_LOGITS_IN if logits_in else 0) | (B.MOE_FLAG_TRAIN if train else 0)
     return B.make_shape(w.T, w.H, w.E, w.K, w.h, w.hs, w.cf,
-                        B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32,
-                        B.MOE_FLAG_LOGITS_IN if logits_in else 0)
+                        B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32, flags)
 
 
 @dataclasses.dataclass
@@ -44,8 +46,9 @@ class MoeBuffers:
     ws: torch.Tensor
 
     @staticmethod
-    def allocate(w: Workload, device="cuda", logits_in: bool = False) -> "MoeBuffers":
-        s = shape_of(w, logits_in)
+    def allocate(w: Workload, device="cuda", logits_in: bool = False,
+                 train: bool = False) -> "MoeBuffers":
+        s = shape_of(w, logits_in, train)
         st = B.moe_check_shape(s)
         if st != B.MOE_OK:
             raise B.MoeError("moe_check_shape", st, B.moe_status_string(st))
@@ -108,3 +111,76 @@ def forward(buf: MoeBuffers, p: dict, stream=None) -> MoeBuffers:
     expert_ffn(buf, p, stream)
     combine(buf, stream)
     return buf
+
+
+@dataclasses.dataclass
+class GradBuffers:
+    """Outputs of the backward calls (weight gradients fp32, the rest in the
+    activation dtype or fp32 as the C ABI states)."""
+    d_out: torch.Tensor
+    d_topk_w: torch.Tensor
+    d_logits: torch.Tensor
+    d_w_router: torch.Tensor
+    d_b_router: torch.Tensor
+    d_xp: torch.Tensor
+    d_w1: torch.Tensor
+    d_w2: torch.Tensor
+    d_x_shared: Optional[torch.Tensor]
+    d_ws1: Optional[torch.Tensor]
+    d_ws2: Optional[torch.Tensor]
+    dx: torch.Tensor
+
+    @staticmethod
+    def allocate(w: Workload, device="cuda") -> "GradBuffers":
+        dt = w.torch_dtype()
+        n = max(B.moe_max_rows(shape_of(w)), 1)
+        f32 = dict(dtype=torch.float32, device=device)
+        act = dict(dtype=dt, device=device)
+        return GradBuffers(
+            d_out=torch.empty((n, w.H), **act),
+            d_topk_w=torch.empty((w.T, w.K), **f32),
+            d_logits=torch.empty((w.T, w.E), **f32),
+            d_w_router=torch.empty((w.H, w.E), **f32),
+            d_b_router=torch.empty((w.E,), **f32),
+            d_xp=torch.empty((n, w.H), **act),
+            d_w1=torch.empty((w.E, w.H, w.h), **f32),
+            d_w2=torch.empty((w.E, w.h, w.H), **f32),
+            d_x_shared=torch.empty((w.T, w.H), **act) if w.hs else None,
+            d_ws1=torch.empty((w.H, w.hs), **f32) if w.hs else None,
+            d_ws2=torch.empty((w.hs, w.H), **f32) if w.hs else None,
+            dx=torch.empty((w.T, w.H), **act),
+        )
+
+
+def combine_backward(buf: MoeBuffers, g: GradBuffers, dy, stream=None):
+    B.moe_combine_backward(buf.shape, dy, buf.out, buf.row_of, buf.topk_w, g.d_out, g.d_topk_w,
+                           stream)
+
+
+def route_backward(buf: MoeBuffers, g: GradBuffers, p: dict, alpha: float, stream=None):
+    B.moe_route_backward(buf.shape, p["x"], buf.logits, buf.topk_ids, buf.topk_w, g.d_topk_w,
+                         buf.counts, alpha, g.d_logits, g.d_w_router, g.d_b_router, buf.ws,
+                         stream)
+
+
+def expert_ffn_backward(buf: MoeBuffers, g: GradBuffers, p: dict, dy, stream=None):
+    B.moe_expert_ffn_backward(buf.shape, buf.xp, buf.offsets, p["w1"], p["w2"], buf.hbuf,
+                              g.d_out, g.d_xp, g.d_w1, g.d_w2, p["x"], p.get("ws1"),
+                              p.get("ws2"), buf.hshared, dy, g.d_x_shared, g.d_ws1, g.d_ws2,
+                              buf.ws, stream)
+
+
+def permute_backward(buf: MoeBuffers, g: GradBuffers, p: dict, stream=None):
+    B.moe_permute_backward(buf.shape, g.d_xp, buf.row_of, g.d_x_shared, g.d_logits, p["w_r"],
+                           g.dx, buf.ws, stream)
+
+
+def backward(buf: MoeBuffers, g: GradBuffers, p: dict, dy, alpha: float = 0.0,
+             stream=None) -> GradBuffers:
+    """combine -> route -> expert FFN -> permute backward, asynchronously,
+    for the gradient of <dy, y> + alpha * aux after a train-mode forward."""
+    combine_backward(buf, g, dy, stream)
+    route_backward(buf, g, p, alpha, stream)
+    expert_ffn_backward(buf, g, p, dy, stream)
+    permute_backward(buf, g, p, stream)
+    return g

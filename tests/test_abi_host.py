@@ -64,7 +64,9 @@ def shape(**kw):
     ({"h_shared": 12}, B.MOE_ERR_UNSUPPORTED),
     ({"h_shared": -8}, B.MOE_ERR_INVALID_ARG),
     ({"dtype": 7}, B.MOE_ERR_INVALID_ARG),
-    ({"flags": 2}, B.MOE_ERR_INVALID_ARG),
+    ({"flags": 4}, B.MOE_ERR_INVALID_ARG),
+    ({"flags": B.MOE_FLAG_TRAIN}, B.MOE_OK),
+    ({"flags": B.MOE_FLAG_TRAIN | B.MOE_FLAG_LOGITS_IN}, B.MOE_OK),
     ({"capacity_factor": float("nan")}, B.MOE_ERR_INVALID_ARG),
     ({"T": 1 << 28, "K": 8, "E": 8}, B.MOE_ERR_UNSUPPORTED),
     ({"K": 8, "E": 256, "T": 1}, B.MOE_OK),
@@ -135,3 +137,49 @@ def test_other_calls_reject_null_and_small_workspace(lib):
     assert lib.moe_combine(ctypes.byref(s), p, p, p, None, None, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(ss), p, p, p, None, p, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(s), p + 4, p, p, None, p, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_train_workspace_holds_preactivations(lib):
+    """MOE_FLAG_TRAIN adds the GELU pre-activations ([max_rows, h_exp] and
+    [T, h_shared] in the dtype) and the backward scratch to the workspace."""
+    s0 = shape(h_shared=64)
+    s1 = shape(h_shared=64, flags=B.MOE_FLAG_TRAIN)
+    extra = B.moe_workspace_size(s1) - B.moe_workspace_size(s0)
+    rows = B.moe_max_rows(s0)
+    assert extra >= 2 * (rows * 128 + 100 * 64)
+
+
+def test_backward_calls_reject_bad_arguments_before_launch(lib):
+    s = shape(flags=B.MOE_FLAG_TRAIN)
+    s_fwd = shape()
+    p = 0x4000
+    big = 1 << 30
+    # combine backward: null / misaligned
+    assert lib.moe_combine_backward(ctypes.byref(s), p, p, p, p, None, p, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(ctypes.byref(s), p + 2, p, p, p, p, p, None) == B.MOE_ERR_INVALID_ARG
+    # route backward: needs MOE_FLAG_TRAIN, a finite alpha, a big enough workspace
+    args = lambda sh, alpha, ws_bytes: (ctypes.byref(sh), p, p, p, p, p, p, alpha, p, p, None, p,
+                                        ws_bytes, None)
+    assert lib.moe_route_backward(*args(s_fwd, 0.0, big)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(*args(s, float("nan"), big)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(*args(s, 0.0, 8)) == B.MOE_ERR_WORKSPACE
+    # expert FFN backward: null weight gradient, missing flag, shared buffers
+    ffn = lambda sh, dw1, ws_bytes, shared_ptr=None: (
+        ctypes.byref(sh), p, p, p, p, p, p, p, dw1, p, shared_ptr, shared_ptr, shared_ptr,
+        shared_ptr, shared_ptr, shared_ptr, shared_ptr, shared_ptr, p, ws_bytes, None)
+    assert lib.moe_expert_ffn_backward(*ffn(s, None, big)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_backward(*ffn(s_fwd, p, big)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_backward(*ffn(s, p, 8)) == B.MOE_ERR_WORKSPACE
+    ss = shape(h_shared=64, flags=B.MOE_FLAG_TRAIN)
+    assert lib.moe_expert_ffn_backward(*ffn(ss, p, big)) == B.MOE_ERR_INVALID_ARG
+    # one expert segment beyond a 2 GiB buffer range is refused
+    huge = shape(T=1 << 17, E=1, K=1, H=8192, h_exp=8192, capacity_factor=0.0,
+                 flags=B.MOE_FLAG_TRAIN)
+    assert lib.moe_expert_ffn_backward(*ffn(huge, p, 1 << 62)) == B.MOE_ERR_UNSUPPORTED
+    # permute backward: d_x_shared required with a shared expert
+    assert lib.moe_permute_backward(ctypes.byref(ss), p, p, None, p, p, p, p, big,
+                                    None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_backward(ctypes.byref(s_fwd), p, p, None, p, p, p, p, big,
+                                    None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_backward(ctypes.byref(s), p, p, None, p, p, p, p, 8,
+                                    None) == B.MOE_ERR_WORKSPACE

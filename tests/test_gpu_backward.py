@@ -1,0 +1,164 @@
+"""GPU parity of the backward pass against the CPU oracle, through the C ABI.
+
+Protocol: seeded inputs and a seeded upstream gradient dy feed both sides;
+the GPU runs the forward with MOE_FLAG_TRAIN and then combine -> route ->
+expert FFN -> permute backward; the oracle differentiates its own float64
+layer (``moe_oracle.backward``) with the routing taken from the GPU's fp32
+logits (the forward's bit-exact routing is checked first).  Every gradient
+must satisfy max|g - g_ref| / max|g_ref| <= 2e-2 in bf16 mode (bf16 operands,
+fp32 accumulation, bf16 intermediates d_out, d_u, d_xp, dx) and <= 1e-4 in
+fp32 mode; d_topk_w and d_logits are fp32 on both sides and take the same
+bound.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_08_amd import binding as B
+from mixture_experts_layer_08_amd import layer
+from mixture_experts_layer_08_amd.inputs import (WORKLOADS, Workload, make_grad_output,
+                                                 make_inputs, sample_tokens)
+from oracle import moe_oracle as O
+from tests.test_gpu_parity import check_routing, f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def relerr(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+def run_train(w: Workload, p: dict, dy, alpha: float):
+    buf = layer.MoeBuffers.allocate(w, train=True)
+    g = layer.GradBuffers.allocate(w)
+    layer.forward(buf, p)
+    layer.backward(buf, g, p, dy, alpha)
+    torch.cuda.synchronize()
+    return buf, g
+
+
+def oracle_backward(w, p, dy, alpha, buf):
+    l = buf.logits.cpu().numpy().astype(np.float64)
+    return O.backward(f64(p["x"]), f64(p["w_r"]), None if p["b_r"] is None else f64(p["b_r"]),
+                      f64(p["w1"]), f64(p["w2"]), None if p["ws1"] is None else f64(p["ws1"]),
+                      None if p["ws2"] is None else f64(p["ws2"]), dy=f64(dy), K=w.K, cf=w.cf,
+                      alpha=alpha, logits=l)
+
+
+def check_all(w, p, dy, alpha, buf, g):
+    check_routing(w, buf)
+    ref = oracle_backward(w, p, dy, alpha, buf)
+    tol = TOL[w.dtype]
+    N = int(buf.offsets[-1].item())
+    pairs = [
+        ("d_topk_w", g.d_topk_w, ref["d_w"]),
+        ("d_logits", g.d_logits, ref["d_logits"]),
+        ("d_w_router", g.d_w_router, ref["dw_r"]),
+        ("d_b_router", g.d_b_router, ref["db_r"]),
+        ("d_out", g.d_out[:N], ref["d_out"]),
+        ("d_xp", g.d_xp[:N], ref["d_xp"]),
+        ("d_w1", g.d_w1, ref["dw1"]),
+        ("d_w2", g.d_w2, ref["dw2"]),
+        ("dx", g.dx, ref["dx"]),
+    ]
+    if w.hs:
+        pairs += [("d_ws1", g.d_ws1, ref["dws1"]), ("d_ws2", g.d_ws2, ref["dws2"])]
+    errs = {}
+    for name, got, want in pairs:
+        errs[name] = relerr(f64(got), want)
+    say(f"{w.name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"relative errors above {tol}: {bad}"
+    return ref
+
+
+@pytest.mark.parametrize("name,alpha", [("tiny_fp32", 0.3), ("small_bf16", 0.01)])
+def test_workload_full_tensors(name, alpha):
+    w = WORKLOADS[name]
+    say(f"backward {name} T={w.T} H={w.H} E={w.E} K={w.K} h={w.h}")
+    p = make_inputs(w, seed=0, device="cuda")
+    dy = make_grad_output(w, seed=0, device="cuda")
+    buf, g = run_train(w, p, dy, alpha)
+    check_all(w, p, dy, alpha, buf, g)
+
+
+EDGE = [
+    # ragged sizes, drops (cf 0.9)
+    Workload("ragged", T=1000, H=200, E=6, K=2, h=136, cf=0.9),
+    # shared expert, random router bias, top-4
+    Workload("shared", T=512, H=128, E=8, K=4, h=64, hs=96, cf=1.25, bias="normal"),
+    # one expert: the dense FFN
+    Workload("dense", T=300, H=64, E=1, K=1, h=96),
+    # the most experts and slots
+    Workload("e256k8", T=300, H=64, E=256, K=8, h=32, cf=1.0),
+    # top-1 with a tight capacity
+    Workload("top1", T=257, H=96, E=5, K=1, h=40, cf=0.5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_edge_cases(w, dtype):
+    w = w.replace(dtype=dtype, name=f"{w.name}_{dtype}")
+    say(f"backward edge {w}")
+    p = make_inputs(w, seed=11, device="cuda")
+    dy = make_grad_output(w, seed=11, device="cuda")
+    buf, g = run_train(w, p, dy, 0.05)
+    check_all(w, p, dy, 0.05, buf, g)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_experts_and_all_dropped_tokens(dtype):
+    """Bias forces every token onto experts 0 and 1 with a tight capacity:
+    empty experts get zero weight gradients, tokens that lose every slot get
+    only the router part of dx."""
+    w = Workload("empty", T=400, H=64, E=8, K=2, h=64, cf=0.5, dtype=dtype)
+    p = make_inputs(w, seed=3, device="cuda")
+    p["b_r"] = torch.zeros(8, device="cuda")
+    p["b_r"][:2] = 100.0
+    dy = make_grad_output(w, seed=3, device="cuda")
+    buf, g = run_train(w, p, dy, 0.2)
+    check_all(w, p, dy, 0.2, buf, g)
+    assert torch.all(g.d_w1[2:] == 0) and torch.all(g.d_w2[2:] == 0)
+
+
+def test_backward_is_deterministic():
+    w = Workload("det", T=700, H=128, E=8, K=2, h=96, hs=64, cf=1.25)
+    p = make_inputs(w, seed=5, device="cuda")
+    dy = make_grad_output(w, seed=5, device="cuda")
+    _, g1 = run_train(w, p, dy, 0.1)
+    _, g2 = run_train(w, p, dy, 0.1)
+    for name in ("d_topk_w", "d_logits", "d_w_router", "d_b_router", "d_w1", "d_w2", "d_ws1",
+                 "d_ws2", "dx"):
+        a, b = getattr(g1, name), getattr(g2, name)
+        assert torch.equal(a, b), name
+
+
+def test_backward_requires_train_flag():
+    w = Workload("noflag", T=64, H=64, E=4, K=2, h=32)
+    p = make_inputs(w, seed=1, device="cuda")
+    buf = layer.MoeBuffers.allocate(w)  # no MOE_FLAG_TRAIN
+    g = layer.GradBuffers.allocate(w)
+    layer.forward(buf, p)
+    with pytest.raises(B.MoeError) as ei:
+        layer.route_backward(buf, g, p, 0.0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
