@@ -10,7 +10,9 @@ cf-1.com page "Dissecting the MoE communication bottleneck", section 2.2).
 Prints one JSON line: tokens/s of the whole forward, the roofline of the
 dominant kernel (the grouped GEMM, timed with HIP events on its launch stream
 over the timed region), permute / combine / router bandwidth, and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  A ``backward`` object
+reports the training step of the same workload separately (a MOE_FLAG_TRAIN
+forward, then the four backward calls); the headline value stays the forward.
 """
 
 from __future__ import annotations
@@ -40,6 +42,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training-step (forward + backward) leg")
+    ap.add_argument("--backward-steps", type=int, default=10)
+    ap.add_argument("--alpha", type=float, default=0.01,
+                    help="aux-loss coefficient of the backward leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run one device copy of BYTES bytes "
                          "(the known-size kernel that calibrates HBM counters)")
@@ -83,6 +90,73 @@ def cpu_baseline(w, p, n_tokens: int):
                    f"numpy oracle forward (router, routing with capacity on the sub-batch, "
                    f"expert FFN, combine) in {dt:.1f} s; BLAS threads {threads}, "
                    f"host cpu_count {os.cpu_count()}"),
+    }
+
+
+def backward_leg(w, p, dev, steps: int, warmup: int, alpha: float) -> dict:
+    """Training step: forward with MOE_FLAG_TRAIN, then combine -> route ->
+    expert FFN -> permute backward, each call bracketed by HIP events on the
+    launch stream."""
+    import torch
+
+    from mixture_experts_layer_08_amd import counters, layer
+    from mixture_experts_layer_08_amd.inputs import make_grad_output
+
+    buf = layer.MoeBuffers.allocate(w, device=dev, train=True)
+    g = layer.GradBuffers.allocate(w, device=dev)
+    dy = make_grad_output(w, seed=0, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward(buf, p, stream)
+        layer.backward(buf, g, p, dy, alpha, stream)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(6)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        m = marks[s]
+        m[0].record(stream)
+        layer.forward(buf, p, stream)
+        m[1].record(stream)
+        layer.combine_backward(buf, g, dy, stream)
+        m[2].record(stream)
+        layer.route_backward(buf, g, p, alpha, stream)
+        m[3].record(stream)
+        layer.expert_ffn_backward(buf, g, p, dy, stream)
+        m[4].record(stream)
+        layer.permute_backward(buf, g, p, stream)
+        m[5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def stage_ms(i):
+        return sum(marks[s][i].elapsed_time(marks[s][i + 1]) for s in range(steps)) / steps
+
+    fwd_ms, comb_ms, route_ms, ffn_ms, perm_ms = (stage_ms(i) for i in range(5))
+    N = int(buf.offsets[-1].item())
+    b = 2 if w.dtype == "bf16" else 4
+    # four GEMMs per expert FFN backward (d u, d W2, d W1, d xp), 2*N*H*h each
+    flop = 4 * counters.grouped_gemm_flop_per_launch(N, w.H, w.h)
+    if w.hs:
+        flop += 4 * counters.grouped_gemm_flop_per_launch(w.T, w.H, w.hs)
+    comb_bytes = w.T * w.H * b + 2 * N * w.H * b
+    perm_bytes = N * w.H * b + w.T * w.H * b * (3 if w.hs else 2)
+    step_ms = wall * 1e3 / steps
+    return {
+        "training_tokens_per_s": w.T / (step_ms * 1e-3),
+        "ms_per_training_step": step_ms,
+        "steps": steps,
+        "alpha": alpha,
+        "stages_ms": {"forward_train": fwd_ms, "combine_backward": comb_ms,
+                      "route_backward": route_ms, "expert_ffn_backward": ffn_ms,
+                      "permute_backward": perm_ms},
+        "expert_ffn_backward_tflops": flop / (ffn_ms * 1e-3) / 1e12,
+        "expert_ffn_backward_frac_of_peak": flop / (ffn_ms * 1e-3) / 1e12 /
+        (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),
+        "combine_backward_GBs": comb_bytes / (comb_ms * 1e-3) / 1e9,
+        "permute_backward_GBs": perm_bytes / (perm_ms * 1e-3) / 1e9,
+        "note": "expert_ffn_backward: d u (NT + GELU'), d W2 and d W1 (TN, fp32 out), d xp (NT); "
+                "permute_backward includes the d_logits W_r^T GEMM accumulated into dx",
     }
 
 
@@ -191,6 +265,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not a.no_backward:
+        del buf
+        torch.cuda.empty_cache()
+        res["backward"] = backward_leg(w, p, dev, a.backward_steps, min(a.warmup, 3), a.alpha)
     if a.copy_calibration > 0:
         n = a.copy_calibration // 4
         src = torch.empty(n, dtype=torch.float32, device=dev)

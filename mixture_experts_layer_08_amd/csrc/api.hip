@@ -22,7 +22,7 @@ struct WsLayout {
   // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
   // weight gradient's partials, and bf16 copies of d_logits / W_r padded to
   // a multiple of 8 experts for the d_logits * W_r^T GEMM
-  size_t preact, preact_sh, part, dbpart, dl8, wr8;
+  size_t preact, preact_sh, part, dbpart, dl8, wr8, chunk_off;
   size_t total;
 };
 
@@ -47,19 +47,21 @@ WsLayout ws_layout(const moe_shape* s) {
   off += align_up((size_t)s->T * s->K * 4);
   if (s->flags & MOE_FLAG_TRAIN) {
     const size_t elem = s->dtype == MOE_BF16 ? 2 : 4;
-    const size_t nch = (size_t)route_bwd_chunks(s->T);
+    const size_t nch = (size_t)route_bwd_chunks(s->T, s->E);
     L.preact = off;
     off += align_up((size_t)max_rows_of(s) * s->h_exp * elem);
     L.preact_sh = off;
     off += align_up((size_t)s->T * s->h_shared * elem);
     L.part = off;
-    off += align_up(nch * s->H * s->E * 4);
+    off += align_up(nch * s->H * pad8(s->E) * 4);
     L.dbpart = off;
-    off += align_up(nch * s->E * 4);
+    off += align_up((size_t)((s->T + 63) / 64) * s->E * 4);  // 64-token blocks
     L.dl8 = off;
     if (s->dtype == MOE_BF16) off += align_up((size_t)s->T * pad8(s->E) * 2);
     L.wr8 = off;
     if (s->dtype == MOE_BF16) off += align_up((size_t)s->H * pad8(s->E) * 2);
+    L.chunk_off = off;
+    off += align_up((nch + 1) * 4);
   }
   L.total = off;
   return L;
@@ -368,6 +370,8 @@ moe_status moe_route_backward(const moe_shape* s, const void* x, const float* lo
   a.d_b_router = d_b_router;
   a.part = at<float>(ws, L.part);
   a.dbpart = at<float>(ws, L.dbpart);
+  a.dl16 = at<bf16>(ws, L.dl8);  // the padded bf16 d_logits (also used by moe_permute_backward)
+  a.chunk_off = at<int32_t>(ws, L.chunk_off);
   a.T = s->T;
   a.H = s->H;
   a.E = s->E;

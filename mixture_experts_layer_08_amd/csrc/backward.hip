@@ -12,6 +12,8 @@
 //
 // Every reduction runs in a fixed order (wave butterflies, slot order,
 // token-chunk order), so results are deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -190,83 +192,183 @@ __global__ __launch_bounds__(256) void k_route_bwd_dl(
   }
 }
 
-// Router weight gradient, first pass: per token chunk c (kRouteBwdChunk
-// tokens) and expert group g (32 experts), thread h of the workgroup's 256
-// columns accumulates part[c][h][e] = sum_{t in c} x[t,h] d_l[t,e] in token
-// order; the x-column-0 workgroup also sums d_l (db partials).  A 64-token
-// slice of d_l[:, group] is staged in LDS and read as a broadcast.
-template <bool BF16>
+// Router weight gradient, first pass: per token chunk c (route_bwd_chunk(E)
+// tokens) and expert group g (EG experts), thread i of the workgroup owns
+// columns h, h+1 (h = 2i + 512 blockIdx.x) and accumulates
+// part[c][h][e] = sum_{t in c} x[t,h] d_l[t,e] in token order.  d_l for 256
+// tokens at a time is staged in LDS (zero past the chunk and past E) and
+// read as a broadcast.  x is read in double-buffered batches of U tokens
+// from clamped addresses and kept raw until its batch is multiplied, so 2U
+// loads per lane stay in flight; columns past H compute on column 0 and are
+// never stored.
+template <bool BF16, int EG>
 __global__ __launch_bounds__(256) void k_route_bwd_dw_part(
     const void* __restrict__ xv, const float* __restrict__ d_logits, float* __restrict__ part,
-    float* __restrict__ dbpart, int T, int H, int E) {
-  __shared__ float s_dl[64][33];
+    int T, int H, int E, int chunk) {
+  constexpr int U = 16;
+  constexpr int SUB = 256;  // tokens per staged slice of d_l
+  static_assert(SUB % (2 * U) == 0, "whole double batches per slice");
+  __shared__ __attribute__((aligned(16))) float s_dl[SUB][EG];
+  using Raw = typename std::conditional<BF16, uint32_t, float2>::type;
   const int tid = threadIdx.x;
-  const int h = blockIdx.x * 256 + tid;
-  const int c = blockIdx.y, g = blockIdx.z;
-  const int e0 = g * 32;
-  const int t_begin = c * kRouteBwdChunk, t_end = min(T, t_begin + kRouteBwdChunk);
-  float acc[32];
+  const int h = blockIdx.x * 512 + 2 * tid;
+  const bool h_ok = h < H;  // H is a multiple of 8: h < H implies h + 1 < H
+  const int hc = h_ok ? h : 0;
+  const int c = blockIdx.y;
+  const int e0 = blockIdx.z * EG;
+  const int t_begin = c * chunk, t_end = min(T, t_begin + chunk);
+  float acc0[EG], acc1[EG];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
-  float db = 0.0f;
-  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
+  for (int j = 0; j < EG; ++j) acc0[j] = acc1[j] = 0.0f;
+  auto load = [&](int t, Raw* r) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = tid + 256 * q;
-      const int tt = i >> 5, j = i & 31;
-      const int t = t0 + tt, e = e0 + j;
+    for (int u = 0; u < U; ++u) {
+      const size_t at = (size_t)min(t + u, T - 1) * H + hc;
+      if constexpr (BF16) r[u] = *(const uint32_t*)((const bf16*)xv + at);
+      else r[u] = *(const float2*)((const float*)xv + at);
+    }
+  };
+  auto accumulate = [&](int tt, const Raw* r) {  // tt: token offset in the slice
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a, b;
+      if constexpr (BF16) {
+        a = bf16_bits_to_f32(r[u] & 0xffffu);
+        b = bf16_bits_to_f32(r[u] >> 16);
+      } else {
+        a = r[u].x;
+        b = r[u].y;
+      }
+#pragma unroll
+      for (int j = 0; j < EG; j += 4) {
+        const f32x4 g = *(const f32x4*)&s_dl[tt + u][j];  // broadcast read
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc0[j + q] = fmaf(a, g[q], acc0[j + q]);
+          acc1[j + q] = fmaf(b, g[q], acc1[j + q]);
+        }
+      }
+    }
+  };
+  for (int s0 = t_begin; s0 < t_end; s0 += SUB) {
+    __syncthreads();  // the previous slice is no longer read
+    for (int i = tid; i < SUB * EG; i += 256) {
+      const int tt = i / EG, j = i % EG;
+      const int t = s0 + tt, e = e0 + j;
       s_dl[tt][j] = (t < t_end && e < E) ? d_logits[(size_t)t * E + e] : 0.0f;
     }
     __syncthreads();
-    const int nt = min(64, t_end - t0);
-    for (int tt0 = 0; tt0 < nt; tt0 += 8) {
-      float xs[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = t0 + tt0 + u;
-        float v = 0.0f;
-        if (h < H && tt0 + u < nt) {
-          if (BF16) v = (float)((const bf16*)xv)[(size_t)t * H + h];
-          else v = ((const float*)xv)[(size_t)t * H + h];
-        }
-        xs[u] = v;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int j = 0; j < 32; ++j) acc[j] = fmaf(xs[u], s_dl[tt0 + u][j], acc[j]);
+    const int n = min(SUB, t_end - s0);  // tokens of this slice; past them d_l is 0
+    // Straight-line batches (a branch around a load would make the compiler
+    // wait for every load in flight): loads past the slice read clamped rows
+    // and multiply staged zeros; tt + U + u < SUB since tt <= SUB - 2U.
+    // sched_barrier(0) keeps the scheduler from sinking a batch's loads below
+    // the FMAs of the batch before it.
+    Raw r0[U], r1[U];
+    load(s0, r0);
+    for (int tt = 0; tt < n; tt += 2 * U) {
+      load(s0 + tt + U, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(tt, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(s0 + tt + 2 * U, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(tt + U, r1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (blockIdx.x == 0 && tid < 32)
-      for (int tt = 0; tt < nt; ++tt) db += s_dl[tt][tid];
-    __syncthreads();
   }
-  if (h < H) {
+  if (h_ok) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (e0 + j < E) part[((size_t)c * H + h) * E + e0 + j] = acc[j];
+    for (int j = 0; j < EG; ++j) {
+      if (e0 + j < E) {
+        part[((size_t)c * H + h) * E + e0 + j] = acc0[j];
+        part[((size_t)c * H + h + 1) * E + e0 + j] = acc1[j];
+      }
+    }
   }
-  if (blockIdx.x == 0 && tid < 32 && e0 + tid < E) dbpart[(size_t)c * E + e0 + tid] = db;
 }
 
-// Second pass: d_w_router[h][e] = sum_c part[c][h][e] in chunk order, and
-// d_b_router[e] likewise from the db partials.
+// Router bias gradient, first pass: dbpart[b][e] = sum_{t in block b} d_l[t,e]
+// over blocks of kDbBlock tokens.  G = 256 / E_pad threads per expert (E_pad =
+// E rounded up to a power of two): thread (g, e) sums tokens g, g+G, ... of
+// the block in order (a fixed trip count, so its loads are issued together),
+// then a fixed-shape tree over g combines them.
+constexpr int kDbBlock = 64;
+__global__ __launch_bounds__(256) void k_route_bwd_db_part(const float* __restrict__ d_logits,
+                                                           float* __restrict__ dbpart, int T,
+                                                           int E) {
+  __shared__ float s[256];
+  int e_pad = 1;
+  while (e_pad < E) e_pad <<= 1;
+  const int G = 256 / e_pad;  // 1 .. 256, a power of two
+  const int tid = threadIdx.x;
+  const int g = tid / e_pad, e = tid % e_pad;
+  const int t0 = blockIdx.x * kDbBlock;
+  float v = 0.0f;
+  if (e < E) {
+    float x[kDbBlock];
+#pragma unroll
+    for (int i = 0; i < kDbBlock; ++i) {
+      const int t = t0 + g + i * G;
+      x[i] = (i * G < kDbBlock && t < T) ? d_logits[(size_t)t * E + e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kDbBlock; ++i) v += x[i];
+  }
+  s[tid] = v;
+  __syncthreads();
+  for (int w = G >> 1; w > 0; w >>= 1) {
+    if (g < w) s[tid] += s[tid + w * e_pad];
+    __syncthreads();
+  }
+  if (g == 0 && e < E) dbpart[(size_t)blockIdx.x * E + e] = s[tid];
+}
+
+// Token-chunk bounds [c * chunk, min(T, (c+1) * chunk)) as a segment table for
+// the grouped GEMM (the MFMA form of the router weight gradient).
+__global__ void k_chunk_offsets(int32_t* __restrict__ off, int nchunk, int chunk, int T) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i <= nchunk) off[i] = min(i * chunk, T);
+}
+
+// Second pass: d_w_router[h][e] = sum_c part[c][h][e] in chunk order (or,
+// from the MFMA form, sum_c part[c][e][h] with rows of E_ld).
 __global__ __launch_bounds__(256) void k_route_bwd_reduce(const float* __restrict__ part,
-                                                          const float* __restrict__ dbpart,
-                                                          float* __restrict__ d_w,
-                                                          float* __restrict__ d_b, int nchunk,
-                                                          int H, int E) {
+                                                          float* __restrict__ d_w, int nchunk,
+                                                          int H, int E, int e_ld) {
   const size_t n = (size_t)H * E;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
     float s = 0.0f;
-    for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * n + i];
-    d_w[i] = s;
-  } else if (d_b && i < n + E) {
-    const int e = (int)(i - n);
-    float s = 0.0f;
-    for (int c = 0; c < nchunk; ++c) s += dbpart[(size_t)c * E + e];
-    d_b[e] = s;
+    if (e_ld == 0) {
+      for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * n + i];
+      d_w[i] = s;
+    } else {
+      // consecutive threads read consecutive h of one expert's row
+      const int e = (int)(i / H), h = (int)(i % H);
+      const size_t cs = (size_t)e_ld * H;
+      for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * cs + i];
+      d_w[(size_t)h * E + e] = s;
+    }
   }
+}
+
+// d_b_router[e] = sum_b dbpart[b][e]: one workgroup per expert; thread j
+// sums blocks j, j+256, ... in order, then a fixed-shape tree.
+__global__ __launch_bounds__(256) void k_route_bwd_db_reduce(const float* __restrict__ dbpart,
+                                                             float* __restrict__ d_b, int ndb,
+                                                             int E) {
+  __shared__ float s[256];
+  const int e = blockIdx.x, j = threadIdx.x;
+  float v = 0.0f;
+  for (int b = j; b < ndb; b += 256) v += dbpart[(size_t)b * E + e];
+  s[j] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (j < w) s[j] += s[j + w];
+    __syncthreads();
+  }
+  if (j == 0) d_b[e] = s[0];
 }
 
 // One wave per token: dx[t] = sum_{k kept} d_xp[row_of[t,k]] (+ d_x_shared[t])
@@ -358,18 +460,56 @@ hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st) {
                                                   a.counts, a.alpha, a.d_logits, a.T, a.E, a.K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nchunk = route_bwd_chunks(a.T);
-  const dim3 grid((a.H + 255) / 256, nchunk, (a.E + 31) / 32);
-  if (a.bf16)
-    k_route_bwd_dw_part<true><<<grid, 256, 0, st>>>(a.x, a.d_logits, a.part, a.dbpart, a.T, a.H,
-                                                     a.E);
-  else
-    k_route_bwd_dw_part<false><<<grid, 256, 0, st>>>(a.x, a.d_logits, a.part, a.dbpart, a.T,
-                                                      a.H, a.E);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t n = (size_t)a.H * a.E + a.E;
-  k_route_bwd_reduce<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.part, a.dbpart, a.d_w_router,
-                                                                  a.d_b_router, nchunk, a.H, a.E);
+  const int chunk = route_bwd_chunk(a.E);
+  const int nchunk = route_bwd_chunks(a.T, a.E);
+  int e_ld = 0;  // partials [c][H][E] (0) or [c][e_ld][H] (MFMA form)
+  if (route_bwd_uses_mfma(a.bf16, a.E)) {
+    // d_w_router^T, chunk by chunk: a TN grouped GEMM whose segments are the
+    // token chunks, A = d_l in bf16 padded to E8 experts [T][E8], B = x [T][H]
+    const int E8 = (a.E + 7) & ~7;
+    k_chunk_offsets<<<(nchunk + 256) / 256, 256, 0, st>>>(a.chunk_off, nchunk, chunk, a.T);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_pad_bf16(a.d_logits, true, a.dl16, a.T, a.E, E8, st)) != hipSuccess) return e;
+    GemmArgs g;
+    g.layout = kGemmTN;
+    g.epi = kEpiStore;
+    g.A = a.dl16;
+    g.B = a.x;
+    g.C = a.part;
+    g.offsets = a.chunk_off;
+    g.G = nchunk;
+    g.M = E8;
+    g.N = a.H;
+    if ((e = launch_grouped_gemm_bf16(g, st)) != hipSuccess) return e;
+    e_ld = E8;
+  } else {
+    // expert groups of 8, 16 or 32 (the widest that E fills)
+    const int EG = a.E <= 8 ? 8 : (a.E <= 16 ? 16 : 32);
+    const dim3 grid((a.H + 511) / 512, nchunk, (a.E + EG - 1) / EG);
+#define MOE_DW_PART(BF, EGV) \
+  k_route_bwd_dw_part<BF, EGV><<<grid, 256, 0, st>>>(a.x, a.d_logits, a.part, a.T, a.H, a.E, chunk)
+    if (a.bf16) {
+      if (EG == 8) MOE_DW_PART(true, 8);
+      else if (EG == 16) MOE_DW_PART(true, 16);
+      else MOE_DW_PART(true, 32);
+    } else {
+      if (EG == 8) MOE_DW_PART(false, 8);
+      else if (EG == 16) MOE_DW_PART(false, 16);
+      else MOE_DW_PART(false, 32);
+    }
+#undef MOE_DW_PART
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.d_b_router) {
+    const int ndb = (a.T + kDbBlock - 1) / kDbBlock;
+    k_route_bwd_db_part<<<ndb, 256, 0, st>>>(a.d_logits, a.dbpart, a.T, a.E);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_route_bwd_db_reduce<<<a.E, 256, 0, st>>>(a.dbpart, a.d_b_router, ndb, a.E);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const size_t n = (size_t)a.H * a.E;
+  k_route_bwd_reduce<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.part, a.d_w_router, nchunk,
+                                                                  a.H, a.E, e_ld);
   return hipGetLastError();
 }
 

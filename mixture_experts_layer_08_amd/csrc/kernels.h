@@ -111,10 +111,13 @@ struct CombineBwdArgs {
 };
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st);
 
-// Tokens per chunk of the router weight gradient's first pass; its partials
-// are [chunks][H][E] fp32.
-constexpr int kRouteBwdChunk = 1024;
-inline int route_bwd_chunks(int T) { return (T + kRouteBwdChunk - 1) / kRouteBwdChunk; }
+// Tokens per chunk of the router weight gradient's first pass (wider for
+// many experts, so that its fp32 partials [chunks][H][E] stay small).
+inline int route_bwd_chunk(int E) { return E <= 32 ? 512 : (E <= 64 ? 1024 : 2048); }
+inline int route_bwd_chunks(int T, int E) { return (T + route_bwd_chunk(E) - 1) / route_bwd_chunk(E); }
+// bf16 mode with more than 32 experts computes the router weight gradient on
+// MFMA (a TN grouped GEMM over token chunks), else on the vector ALUs.
+inline bool route_bwd_uses_mfma(bool bf16, int E) { return bf16 && E > 32; }
 
 struct RouteBwdArgs {
   bool bf16;
@@ -128,8 +131,10 @@ struct RouteBwdArgs {
   float* d_logits;
   float* d_w_router;
   float* d_b_router;   // nullable
-  float* part;         // [chunks][H][E] scratch
-  float* dbpart;       // [chunks][E] scratch
+  float* part;         // [chunks][H][E] (or [chunks][E8][H], MFMA form) scratch
+  float* dbpart;       // [ceil(T / 64)][E] scratch
+  ::moe::bf16* dl16;   // [T][E8] scratch (MFMA form)
+  int32_t* chunk_off;  // [chunks + 1] scratch (MFMA form)
   int T, H, E, K;
 };
 hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
