@@ -162,3 +162,91 @@ def test_backward_requires_train_flag():
     with pytest.raises(B.MoeError) as ei:
         layer.route_backward(buf, g, p, 0.0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_mixtral_full_size_sampled():
+    """The bench's training step at full size (T=32768, H=4096, E=8, top-2,
+    h=14336), in the bench's launch configuration.  The oracle cannot run
+    the whole backward here, so it checks what it can compute exactly:
+      - d_logits, d_w_router, d_b_router in full, from the oracle's gate
+        gradient applied to the GPU's d_topk_w (as the routing comparison
+        starts from the GPU's logits);
+      - d_topk_w and dx on 64 seeded tokens (each token's values depend
+        only on its own rows once routing and d_logits are fixed);
+      - 64 entries each of d_w1 and d_w2 of two experts, from column
+        slices computed over the whole segment (matrix-vector products)."""
+    w = WORKLOADS["mixtral_bf16"]
+    alpha = 0.01
+    say(f"[{w.name}] full-size backward parity (sampled)")
+    p = make_inputs(w, seed=0, device="cuda")
+    dy = make_grad_output(w, seed=0, device="cuda")
+    buf, g = run_train(w, p, dy, alpha)
+    r = check_routing(w, buf)
+    f32 = lambda t: t.detach().to("cpu").to(torch.float32).numpy()
+    x = f32(p["x"])
+    wr = f32(p["w_r"]).astype(np.float64)
+    dyh = f32(dy)
+    l = buf.logits.cpu().numpy().astype(np.float64)
+    d_tw = g.d_topk_w.cpu().numpy().astype(np.float64)
+    tol = TOL["bf16"]
+
+    # gate gradient from the GPU's d_topk_w; router weight and bias in full
+    dl = O.route_backward(l, r["ids"], r["w"], d_tw, w.E, w.K, alpha)
+    errs = {"d_logits": relerr(g.d_logits.cpu().numpy(), dl)}
+    errs["d_w_router"] = relerr(g.d_w_router.cpu().numpy(), x.T.astype(np.float64) @ dl)
+    errs["d_b_router"] = relerr(g.d_b_router.cpu().numpy(), dl.sum(axis=0))
+
+    # sampled tokens: d_topk_w and dx
+    toks = sample_tokens(w.T, 64, seed=3).numpy()
+    row_of = r["row_of"]
+    w1 = [None] * w.E
+    w2 = [None] * w.E
+    def W1(e):
+        if w1[e] is None:
+            w1[e] = f32(p["w1"][e]).astype(np.float64)
+        return w1[e]
+    def W2(e):
+        if w2[e] is None:
+            w2[e] = f32(p["w2"][e]).astype(np.float64)
+        return w2[e]
+    dtw_ref = np.zeros((len(toks), w.K))
+    dx_ref = np.zeros((len(toks), w.H))
+    for n, t in enumerate(toks):
+        xt = x[t].astype(np.float64)
+        for k in range(w.K):
+            if row_of[t, k] < 0:
+                continue
+            e = int(r["ids"][t, k])
+            u = xt @ W1(e)
+            dtw_ref[n, k] = dyh[t].astype(np.float64) @ (O.gelu_tanh(u) @ W2(e))
+            d_out = r["w"][t, k] * dyh[t].astype(np.float64)
+            du = (d_out @ W2(e).T) * O.gelu_tanh_grad(u)
+            dx_ref[n] += du @ W1(e).T
+        dx_ref[n] += dl[t] @ wr.T
+    errs["d_topk_w (sampled)"] = relerr(d_tw[toks], dtw_ref)
+    errs["dx (sampled)"] = relerr(f32(g.dx)[toks], dx_ref)
+
+    # sampled weight-gradient entries of experts 0 and E-1
+    rng = np.random.default_rng(5)
+    off = r["offsets"]
+    for e in (0, w.E - 1):
+        rows = np.arange(off[e], off[e + 1])
+        toks_e = r["token_of"][rows]
+        slot = np.array([int(np.nonzero(row_of[t] == rr)[0][0]) for t, rr in zip(toks_e, rows)])
+        we = r["w"][toks_e, slot][:, None]
+        xe = x[toks_e].astype(np.float64)
+        d_out_e = we * dyh[toks_e].astype(np.float64)
+        js = rng.choice(w.h, 8, replace=False)
+        is_ = rng.choice(w.H, 8, replace=False)
+        u = xe @ W1(e)[:, js]                      # [rows, 8]
+        gcol = O.gelu_tanh(u)
+        du = (d_out_e @ W2(e)[js, :].T) * O.gelu_tanh_grad(u)
+        dw2_ref = gcol.T @ d_out_e[:, is_]         # [8 j, 8 i]
+        dw1_ref = xe[:, is_].T @ du                # [8 i, 8 j]
+        dw2_got = g.d_w2[e][js][:, is_].cpu().numpy()
+        dw1_got = g.d_w1[e][is_][:, js].cpu().numpy()
+        errs[f"d_w2[{e}] (sampled)"] = relerr(dw2_got, dw2_ref)
+        errs[f"d_w1[{e}] (sampled)"] = relerr(dw1_got, dw1_ref)
+    say("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"relative errors above {tol}: {bad}"
