@@ -20,9 +20,11 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_KERNEL = "k_grouped_gemm_bf16"
+# the forward's row-major (NN) instantiations: GEMM1 with GELU and GEMM2
+GEMM_KERNEL = re.compile(r"k_grouped_gemm_bf16<\s*0\s*,")
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
 
@@ -51,7 +53,7 @@ def traffic(fetch_csv, write_csv, copy_bytes, workload, out):
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
                                 ("write", write_csv, "WRITE_SIZE")):
         d = per_dispatch(path, counter)
-        gemm_ids = [i for i, (k, g, v) in d.items() if GEMM_KERNEL in k]
+        gemm_ids = [i for i, (k, g, v) in d.items() if GEMM_KERNEL.search(k)]
         if not gemm_ids:
             raise SystemExit(f"{path}: no grouped-GEMM dispatch")
         gemms = [d[i][2] for i in gemm_ids]
