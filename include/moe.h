@@ -201,6 +201,104 @@ moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_o
 
 
 /*
+ * MXFP8 forward ([comm] 5.3: dispatch and combine carry the hidden states in
+ * FP8 instead of bf16, halving their bytes; [comm] 5.4: the quantise /
+ * dequantise work must stay cheap; [comm] 4.2: FP8 expert weights).  The
+ * page fixes no FP8 variant or scaling; this library uses MXFP8 from the OCP
+ * Microscaling (MX) specification 1.0: OCP E4M3 elements (largest finite
+ * value 448) in blocks of 32 consecutive values that share one E8M0 scale
+ * 2^X, X = floor(log2 max|v|) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block), stored as the byte X + 127; element = E4M3(v / 2^X),
+ * round to nearest even, magnitudes past 448 saturating to 448.  Blocks run
+ * along the contraction dimension of the GEMM that reads the tensor.
+ *
+ * Routing (moe_route, moe_aux_loss) is unchanged and runs on the bf16 x; the
+ * FP8 calls replace moe_permute, moe_expert_ffn and moe_combine.  Shapes:
+ * dtype MOE_BF16, H, h_exp and h_shared multiples of 64, no MOE_FLAG_TRAIN
+ * (forward only), else MOE_ERR_UNSUPPORTED; each FP8 tensor under 2 GiB.
+ *
+ * Scale layouts (byte tensors):
+ *   operand layout, for an R x Kd tensor that a GEMM reads as its A or B
+ *     operand: [ceil(Kd/128)][R][4]; byte (q, r, j) is the scale of block
+ *     4q + j of row r.  Size: moe_mx_operand_scale_bytes(R, Kd).  Bytes of
+ *     blocks past Kd/32 are neither written nor read.
+ *   row layout, for a tensor that combine reads: [R][cols/32].
+ * Codes are row-major [R][cols] bytes.  Code pointers must be 16-byte
+ * aligned, scale pointers 4-byte aligned.
+ */
+
+/* Bytes of an operand-layout scale tensor for `rows` x `cols` values. */
+size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols);
+
+/*
+ * moe_quantize_weights_mxfp8 - expert weights to MXFP8, once, outside the
+ * forward ([comm] 4.2).
+ *
+ *   w       [batch,K,N]  weights (dtype MOE_BF16 or MOE_F32), K the
+ *                        contraction dimension (H for W1, h for W2)
+ *   q       [batch,N,K]  out: E4M3 codes, transposed so K is contiguous
+ *   scales  [batch,ceil(K/128),N,4]  out: operand layout of each [N,K] slice
+ * K must be a multiple of 64 and N of 32 (MOE_ERR_UNSUPPORTED), N*K < 2^31.
+ */
+moe_status moe_quantize_weights_mxfp8(const void* w, int32_t dtype, int32_t batch, int32_t K,
+                                      int32_t N, uint8_t* q, uint8_t* scales, void* stream);
+
+/*
+ * moe_permute_mxfp8 - moe_permute with the dispatch copy in MXFP8: every
+ * bf16 token row is quantised once and its codes copied to each kept row.
+ * Outputs counts, kept, offsets, row_of, token_of, n_dropped exactly as
+ * moe_permute, plus
+ *   xp_q  [max_rows,H]  E4M3 codes of the packed rows (rows >= N untouched)
+ *   xp_s  operand layout, R = max_rows, Kd = H
+ *   x_q   [T,H], x_s operand layout (R = T): every token's own quantised row,
+ *         for the shared expert; written only when h_shared > 0 (else NULL
+ *         is allowed).
+ */
+moe_status moe_permute_mxfp8(const moe_shape* s, const void* x, const int32_t* topk_ids,
+                             void* ws, size_t ws_bytes, int32_t* counts, int32_t* kept,
+                             int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                             int32_t* n_dropped, uint8_t* xp_q, uint8_t* xp_s, uint8_t* x_q,
+                             uint8_t* x_s, void* stream);
+
+/*
+ * moe_expert_ffn_mxfp8 - the grouped expert FFN on MXFP8 operands ([infra]
+ * 3.3 and 4.2; [comm] 5.1 grouped GEMM, 5.3 FP8): for every row r of
+ * segment e (fp32 accumulation of the block-scaled products),
+ *   h[r]   = MXFP8(GELU_tanh(xp[r] * W1[e]))   -> h_q [max_rows,h_exp] codes,
+ *            h_s operand layout (R = max_rows, Kd = h_exp)
+ *   out[r] = MXFP8(h[r] * W2[e])               -> out_q [max_rows,H] codes,
+ *            out_s row layout [max_rows, H/32]
+ * (each result quantised from its fp32 value in blocks of 32 along the row).
+ *   w1_q, w1_s   moe_quantize_weights_mxfp8 of W1 [E,H,h_exp] (K = H)
+ *   w2_q, w2_s   moe_quantize_weights_mxfp8 of W2 [E,h_exp,H] (K = h_exp)
+ * With h_shared > 0 the same over all T rows of x_q / x_s: hsh_q [T,h_shared]
+ * (operand layout, R = T) and sh_q [T,H] (row layout), from the quantised
+ * Ws1 [1,H,h_shared] and Ws2 [1,h_shared,H]; else those may be NULL.
+ * Rows >= N of h_q / out_q are untouched.
+ */
+moe_status moe_expert_ffn_mxfp8(const moe_shape* s, const uint8_t* xp_q, const uint8_t* xp_s,
+                                const int32_t* offsets, const uint8_t* w1_q,
+                                const uint8_t* w1_s, const uint8_t* w2_q, const uint8_t* w2_s,
+                                uint8_t* h_q, uint8_t* h_s, uint8_t* out_q, uint8_t* out_s,
+                                const uint8_t* x_q, const uint8_t* x_s, const uint8_t* ws1_q,
+                                const uint8_t* ws1_s, const uint8_t* ws2_q,
+                                const uint8_t* ws2_s, uint8_t* hsh_q, uint8_t* hsh_s,
+                                uint8_t* sh_q, uint8_t* sh_s, void* stream);
+
+/*
+ * moe_combine_mxfp8 - y[t] = sum_{k kept} topk_w[t,k] * deq(out[row_of[t,k]])
+ * (+ deq(shared[t])), accumulated in fp32 in slot order, rounded to bf16
+ * ([comm] 1.1 step 4 with [comm] 5.3's FP8 payload).  deq(code) =
+ * E4M3(code) * 2^(scale - 127), exact in fp32.
+ *   out_q, out_s   from moe_expert_ffn_mxfp8 (row layout)
+ *   sh_q, sh_s     shared-expert output (row layout) or NULL
+ *   y [T,H]        bf16 out
+ */
+moe_status moe_combine_mxfp8(const moe_shape* s, const uint8_t* out_q, const uint8_t* out_s,
+                             const int32_t* row_of, const float* topk_w, const uint8_t* sh_q,
+                             const uint8_t* sh_s, void* y, void* stream);
+
+/*
  * Backward pass.  The gradient of L = <dy, y> + alpha * aux by the chain rule
  * of the forward above, for a forward run with MOE_FLAG_TRAIN.  The routing
  * decisions (top-k sets, capacity drops, counts) are held fixed: they are

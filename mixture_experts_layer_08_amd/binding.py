@@ -30,7 +30,9 @@ EXPORTS = (
     "moe_status_string", "moe_check_shape", "moe_capacity", "moe_max_rows",
     "moe_workspace_size", "moe_route", "moe_aux_loss", "moe_permute",
     "moe_expert_ffn", "moe_combine", "moe_combine_backward", "moe_route_backward",
-    "moe_expert_ffn_backward", "moe_permute_backward",
+    "moe_expert_ffn_backward", "moe_permute_backward", "moe_mx_operand_scale_bytes",
+    "moe_quantize_weights_mxfp8", "moe_permute_mxfp8", "moe_expert_ffn_mxfp8",
+    "moe_combine_mxfp8",
 )
 
 
@@ -96,6 +98,17 @@ def lib():
         L.moe_expert_ffn_backward.argtypes = [_SHAPE] + [_P] * 18 + [_SZ, _P]
         L.moe_permute_backward.restype = ctypes.c_int
         L.moe_permute_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_mx_operand_scale_bytes.restype = _SZ
+        L.moe_mx_operand_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.moe_quantize_weights_mxfp8.restype = ctypes.c_int
+        L.moe_quantize_weights_mxfp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+        L.moe_permute_mxfp8.restype = ctypes.c_int
+        L.moe_permute_mxfp8.argtypes = [_SHAPE, _P, _P, _P, _SZ] + [_P] * 10 + [_P]
+        L.moe_expert_ffn_mxfp8.restype = ctypes.c_int
+        L.moe_expert_ffn_mxfp8.argtypes = [_SHAPE] + [_P] * 21 + [_P]
+        L.moe_combine_mxfp8.restype = ctypes.c_int
+        L.moe_combine_mxfp8.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -206,3 +219,36 @@ def moe_permute_backward(s, d_xp, row_of, d_x_shared, d_logits, w_router, dx, ws
     _check("moe_permute_backward", lib().moe_permute_backward(
         ctypes.byref(s), _ptr(d_xp), _ptr(row_of), _ptr(d_x_shared), _ptr(d_logits),
         _ptr(w_router), _ptr(dx), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_mx_operand_scale_bytes(rows: int, cols: int) -> int:
+    return lib().moe_mx_operand_scale_bytes(int(rows), int(cols))
+
+
+def moe_quantize_weights_mxfp8(w, dtype, batch, K, N, q, scales, stream=None):
+    _check("moe_quantize_weights_mxfp8", lib().moe_quantize_weights_mxfp8(
+        _ptr(w), int(dtype), int(batch), int(K), int(N), _ptr(q), _ptr(scales), _stream(stream)))
+
+
+def moe_permute_mxfp8(s, x, topk_ids, ws, counts, kept, offsets, row_of, token_of, n_dropped,
+                      xp_q, xp_s, x_q, x_s, stream=None):
+    _check("moe_permute_mxfp8", lib().moe_permute_mxfp8(
+        ctypes.byref(s), _ptr(x), _ptr(topk_ids), _ptr(ws), _nbytes(ws), _ptr(counts),
+        _ptr(kept), _ptr(offsets), _ptr(row_of), _ptr(token_of), _ptr(n_dropped), _ptr(xp_q),
+        _ptr(xp_s), _ptr(x_q), _ptr(x_s), _stream(stream)))
+
+
+def moe_expert_ffn_mxfp8(s, xp_q, xp_s, offsets, w1_q, w1_s, w2_q, w2_s, h_q, h_s, out_q, out_s,
+                         x_q, x_s, ws1_q, ws1_s, ws2_q, ws2_s, hsh_q, hsh_s, sh_q, sh_s,
+                         stream=None):
+    _check("moe_expert_ffn_mxfp8", lib().moe_expert_ffn_mxfp8(
+        ctypes.byref(s), _ptr(xp_q), _ptr(xp_s), _ptr(offsets), _ptr(w1_q), _ptr(w1_s),
+        _ptr(w2_q), _ptr(w2_s), _ptr(h_q), _ptr(h_s), _ptr(out_q), _ptr(out_s), _ptr(x_q),
+        _ptr(x_s), _ptr(ws1_q), _ptr(ws1_s), _ptr(ws2_q), _ptr(ws2_s), _ptr(hsh_q), _ptr(hsh_s),
+        _ptr(sh_q), _ptr(sh_s), _stream(stream)))
+
+
+def moe_combine_mxfp8(s, out_q, out_s, row_of, topk_w, sh_q, sh_s, y, stream=None):
+    _check("moe_combine_mxfp8", lib().moe_combine_mxfp8(
+        ctypes.byref(s), _ptr(out_q), _ptr(out_s), _ptr(row_of), _ptr(topk_w), _ptr(sh_q),
+        _ptr(sh_s), _ptr(y), _stream(stream)))

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "backward.hip", "api.hip"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_mx8.hip", "mxfp8.hip", "combine.hip",
+           "backward.hip", "api.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -7,6 +7,7 @@
 
 #include "../../include/moe.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace {
 
@@ -112,6 +113,36 @@ GemmArgs tn_gemm(const void* A, const void* B, float* C, const int32_t* offsets,
   g.G = G;
   g.fixed_rows = fixed_rows;
   g.M = M;
+  g.N = N;
+  return g;
+}
+
+// The MXFP8 forward: bf16 tokens, hidden sizes that are whole 64-value
+// K-steps of the FP8 GEMM, no training mode (the FP8 path is forward only),
+// and byte offsets of every FP8 tensor inside the 2 GiB a buffer descriptor
+// addresses.
+moe_status check_mx_shape(const moe_shape* s);
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+MxGemmArgs mx_gemm(int epi, const uint8_t* A, const uint8_t* As, int a_ld, const uint8_t* B,
+                   const uint8_t* Bs, uint8_t* C, uint8_t* Cs, int c_ld,
+                   const int32_t* offsets, int G, int fixed_rows, int max_rows, int Kd, int N) {
+  MxGemmArgs g;
+  g.epi = epi;
+  g.A = A;
+  g.As = As;
+  g.a_ld = a_ld;
+  g.B = B;
+  g.Bs = Bs;
+  g.C = C;
+  g.Cs = Cs;
+  g.c_ld = c_ld;
+  g.offsets = offsets;
+  g.G = G;
+  g.fixed_rows = fixed_rows;
+  g.max_rows = max_rows;
+  g.Kd = Kd;
   g.N = N;
   return g;
 }
@@ -487,4 +518,155 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
   return hip_status(e);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 forward
+// ---------------------------------------------------------------------------
+
+size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return mx_operand_scale_bytes(rows, cols);
+}
+
+moe_status moe_quantize_weights_mxfp8(const void* w, int32_t dtype, int32_t batch, int32_t K,
+                                      int32_t N, uint8_t* q, uint8_t* scales, void* stream) {
+  if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (batch < 1 || K < 1 || N < 1) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(q) || !aligned4(scales)) return MOE_ERR_INVALID_ARG;
+  if (K % 64 || N % 32) return MOE_ERR_UNSUPPORTED;
+  if ((long long)N * K > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_weight_mx8(w, dtype == MOE_BF16, batch, K, N, q, scales,
+                                               (hipStream_t)stream));
+}
+
+moe_status moe_permute_mxfp8(const moe_shape* s, const void* x, const int32_t* topk_ids,
+                             void* ws, size_t ws_bytes, int32_t* counts, int32_t* kept,
+                             int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                             int32_t* n_dropped, uint8_t* xp_q, uint8_t* xp_s, uint8_t* x_q,
+                             uint8_t* x_s, void* stream) {
+  moe_status st = check_mx_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !counts || !kept || !offsets || !row_of || !token_of || !n_dropped ||
+      !xp_q || !xp_s)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xp_q) || !aligned4(xp_s)) return MOE_ERR_INVALID_ARG;
+  const bool shared = s->h_shared > 0;
+  if (shared && (!x_q || !x_s || !aligned16(x_q) || !aligned4(x_s))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  PermuteMx8Args a{};
+  a.x = x;
+  a.topk_ids = topk_ids;
+  a.hist = at<int32_t>(ws, L.hist);
+  a.lrank = at<int32_t>(ws, L.lrank);
+  a.base = at<int32_t>(ws, L.base);
+  a.counts = counts;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.row_of = row_of;
+  a.token_of = token_of;
+  a.n_dropped = n_dropped;
+  a.xp_q = xp_q;
+  a.xp_s = xp_s;
+  a.xp_ld = (int)moe_max_rows(s);
+  a.x_q = shared ? x_q : nullptr;
+  a.x_s = shared ? x_s : nullptr;
+  a.T = s->T;
+  a.H = s->H;
+  a.E = s->E;
+  a.K = s->K;
+  a.C = (int)moe_capacity(s);
+  return hip_status(launch_permute_mx8(a, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_mxfp8(const moe_shape* s, const uint8_t* xp_q, const uint8_t* xp_s,
+                                const int32_t* offsets, const uint8_t* w1_q,
+                                const uint8_t* w1_s, const uint8_t* w2_q, const uint8_t* w2_s,
+                                uint8_t* h_q, uint8_t* h_s, uint8_t* out_q, uint8_t* out_s,
+                                const uint8_t* x_q, const uint8_t* x_s, const uint8_t* ws1_q,
+                                const uint8_t* ws1_s, const uint8_t* ws2_q,
+                                const uint8_t* ws2_s, uint8_t* hsh_q, uint8_t* hsh_s,
+                                uint8_t* sh_q, uint8_t* sh_s, void* stream) {
+  moe_status st = check_mx_shape(s);
+  if (st != MOE_OK) return st;
+  const void* need[] = {xp_q, xp_s, offsets, w1_q, w1_s, w2_q, w2_s, h_q, h_s, out_q, out_s};
+  for (const void* p : need)
+    if (!p || !aligned4(p)) return MOE_ERR_INVALID_ARG;
+  const void* codes[] = {xp_q, w1_q, w2_q, h_q, out_q};
+  for (const void* p : codes)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  const bool shared = s->h_shared > 0;
+  if (shared) {
+    const void* need_sh[] = {x_q, x_s, ws1_q, ws1_s, ws2_q, ws2_s, hsh_q, hsh_s, sh_q, sh_s};
+    for (const void* p : need_sh)
+      if (!p || !aligned4(p)) return MOE_ERR_INVALID_ARG;
+    const void* codes_sh[] = {x_q, ws1_q, ws2_q, hsh_q, sh_q};
+    for (const void* p : codes_sh)
+      if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  const hipStream_t hs = (hipStream_t)stream;
+  const int max_rows = (int)moe_max_rows(s);
+  // GEMM1 + GELU -> h (operand-layout scales for GEMM2), GEMM2 -> out (row layout for combine)
+  hipError_t e = launch_grouped_gemm_mx8(
+      mx_gemm(kMxEpiGeluQuantOperand, xp_q, xp_s, max_rows, w1_q, w1_s, h_q, h_s, max_rows,
+              offsets, s->E, 0, max_rows, s->H, s->h_exp),
+      hs);
+  if (e == hipSuccess)
+    e = launch_grouped_gemm_mx8(mx_gemm(kMxEpiQuantRows, h_q, h_s, max_rows, w2_q, w2_s, out_q,
+                                        out_s, 0, offsets, s->E, 0, max_rows, s->h_exp, s->H),
+                                hs);
+  if (e == hipSuccess && shared) {
+    e = launch_grouped_gemm_mx8(mx_gemm(kMxEpiGeluQuantOperand, x_q, x_s, s->T, ws1_q, ws1_s,
+                                        hsh_q, hsh_s, s->T, nullptr, 1, s->T, s->T, s->H,
+                                        s->h_shared),
+                                hs);
+    if (e == hipSuccess)
+      e = launch_grouped_gemm_mx8(mx_gemm(kMxEpiQuantRows, hsh_q, hsh_s, s->T, ws2_q, ws2_s,
+                                          sh_q, sh_s, 0, nullptr, 1, s->T, s->T, s->h_shared,
+                                          s->H),
+                                  hs);
+  }
+  return hip_status(e);
+}
+
+moe_status moe_combine_mxfp8(const moe_shape* s, const uint8_t* out_q, const uint8_t* out_s,
+                             const int32_t* row_of, const float* topk_w, const uint8_t* sh_q,
+                             const uint8_t* sh_s, void* y, void* stream) {
+  moe_status st = check_mx_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out_q || !out_s || !row_of || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out_q) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  const bool shared = s->h_shared > 0;
+  if (shared && (!sh_q || !sh_s || !aligned16(sh_q))) return MOE_ERR_INVALID_ARG;
+  CombineMx8Args a{};
+  a.out_q = out_q;
+  a.out_s = out_s;
+  a.row_of = row_of;
+  a.topk_w = topk_w;
+  a.sh_q = shared ? sh_q : nullptr;
+  a.sh_s = shared ? sh_s : nullptr;
+  a.y = y;
+  a.T = s->T;
+  a.H = s->H;
+  a.K = s->K;
+  return hip_status(launch_combine_mx8(a, (hipStream_t)stream));
+}
+
 }  // extern "C"
+
+namespace {
+moe_status check_mx_shape(const moe_shape* s) {
+  const moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->flags & MOE_FLAG_TRAIN) return MOE_ERR_UNSUPPORTED;
+  if (s->H % 64 || s->h_exp % 64 || s->h_shared % 64) return MOE_ERR_UNSUPPORTED;
+  const long long rows = moe_max_rows(s);
+  const long long wide = s->H > s->h_exp ? s->H : s->h_exp;
+  const long long wide_sh = s->H > s->h_shared ? s->H : s->h_shared;
+  if (rows * wide > 0x7ffffff0LL || (long long)s->T * wide_sh > 0x7ffffff0LL ||
+      (long long)s->H * s->h_exp > 0x7ffffff0LL || (long long)s->H * s->h_shared > 0x7ffffff0LL)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace

@@ -1,0 +1,335 @@
+// MXFP8 grouped GEMM over variable-length expert segments:
+//   C[r, :] = quant(act(A[r, :] * B[g]^T))   for every row r of segment g,
+// with A and B in MXFP8 (E4M3 codes, one E8M0 scale per 32 values along the
+// contraction dimension, see mx.h), fp32 accumulation, and an epilogue that
+// quantises the result to MXFP8 again, in blocks of 32 along its row.
+//
+// Method: the per-expert contractions of the MoELayer listing of the
+// dpshk.com "MoE module infra notes" (section 4.2: x W1 -> GELU -> W2), run as
+// one grouped GEMM (section 5.1 of the cf-1.com page "Dissecting the MoE
+// communication bottleneck"), with the FP8 hidden states of section 5.3 of
+// that page.  The quantisation of the GEMM output happens in the epilogue,
+// from the accumulators, so no separate quantise pass reads it back (the
+// cost warning of section 5.4).
+//
+// Design (gfx950): the bf16 kernel's 256 x 256 tile on eight waves (two per
+// SIMD), each wave a 128 x 64 block of 4 x 2 v_mfma_scale_f32_32x32x64_f8f6f4
+// tiles; one K-step is 64 values = 64 bytes per row, so a stage holds the same
+// 32 KiB (A [256][64 B], B [256][64 B], 16-byte chunk c of row r stored at
+// c ^ ((r >> 2) & 3)), filled by LDS-direct loads through a 4-stage ring.
+// The block scales ride in the same ring: every even step's stage also
+// carries one 4-byte word per A row and per B row (the scales of that step
+// and the next), loaded by one LDS-direct dword load per wave.
+//
+// Operand layout of the scaled MFMA (checked on the hardware): lane
+// (r = lane % 32, h = lane / 32) supplies row r; its 32 bytes are the values
+// k = 16h .. 16h+15 and k = 32+16h .. 32+16h+15 of the 64-value step, and its
+// scale operand (byte 0) is the scale of block h (k = 32h .. 32h+31).  Both
+// operands use the same mapping, so with 64-byte K rows lane h reads chunks
+// h and h + 2.  The MFMA runs with the operands swapped (B^T fragment as
+// "A"), so each lane accumulates C^T: per 32 x 32 tile it owns row
+// m = lane % 32 and columns 8 (v / 4) + 4 (lane / 32) + v % 4, i.e. lanes m
+// and m + 32 together hold the 32 columns of the tile, which is one MX block
+// of the output row: the block maximum is one cross-lane max away.
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+#include "mx.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMxBM = 256, kMxBN = 256, kMxBK = 64;  // BK in values (= bytes)
+constexpr int kMxThreads = 512;
+constexpr int kMxDma = 2;  // data LDS-direct loads per operand, per wave, per stage
+constexpr int kMxStages = 4;
+constexpr uint32_t kMxDataBytes = (kMxBM + kMxBN) * kMxBK;     // 32 KiB
+constexpr uint32_t kMxScaleBytes = (kMxBM + kMxBN) * 4;        // 2 KiB
+constexpr uint32_t kMxStageBytes = kMxDataBytes + kMxScaleBytes;
+constexpr size_t kMxSmem = (size_t)kMxStages * kMxStageBytes;  // 136 KiB
+static_assert(kMxSmem <= 160 * 1024, "LDS ring exceeds 160 KiB");
+static_assert(kMxStages == 4, "the wait counts below assume four stages");
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
+__device__ __forceinline__ uint32_t lds_b32(uint32_t addr) { return *(const lds_u32*)(uintptr_t)addr; }
+__device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+__device__ __forceinline__ i32x8 frag(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__device__ __forceinline__ f32x16 mfma_mx8(const i32x8& b, const i32x8& a, const f32x16& c,
+                                           int sb, int sa) {
+  // cbsz = blgp = 0: both operands E4M3; opsel 0: byte 0 of each scale word
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, sb, 0, sa);
+}
+
+}  // namespace
+
+// Epilogues: kMxEpiQuantRows: C = quant(acc), scales in row layout
+// [rows][N/32]; kMxEpiGeluQuantOperand: C = quant(GELU(acc)), scales in
+// operand layout with leading dimension c_ld (the next GEMM's A operand).
+//
+// A: [a_rows][Kd] codes, As operand layout (leading dimension a_ld);
+// B: [G][N][Kd] codes, Bs [G][ceil(Kd/128)][N][4].  Kd is a multiple of 64 and
+// N of 32.  Rows of a tile past its segment are computed from whatever the
+// buffers hold there (even NaN) and never stored; each output row depends on
+// its own A row only.
+template <int EPI>
+__global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, uint8_t* __restrict__ C,
+    uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int G, int fixed_rows,
+    int a_rows, int a_ld, int c_ld, int mt_bound, int Kd, int N) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx[];
+  const int nt_count = (N + kMxBN - 1) / kMxBN;
+  if ((int)blockIdx.x >= mt_bound * nt_count) return;
+  int mt, nt, seg, row0, rows;
+  decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
+  if (!find_segment<kMxBM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int rr = lane & 31, kh = lane >> 5;
+  const int n0 = nt * kMxBN;
+  const int nslab = (Kd + 127) / 128;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem_mx;
+
+  // ---- global -> LDS loaders ----
+  // data: instruction d of this wave covers stage rows 16 (8d + wave) .. +15,
+  // four lanes per 64-byte row; rows past the buffer read as zero.
+  const int r_row_l = lane >> 2;
+  const int r_chunk = mx_swz(r_row_l, lane & 3);
+  const u32x4 ra = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd);
+  const u32x4 rb = make_rsrc_words(B + ((size_t)seg * N + n0) * Kd, (long long)(N - n0) * Kd);
+  const uint32_t d_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 16);
+  const uint32_t d_stride = (uint32_t)(8 * 16 * Kd);
+  // scales: waves 0-3 load A rows 64 w .. +63, waves 4-7 B rows 64 (w-4) ..
+  // +63; lane l fetches the word of row (.. + l) of slab s / 2.
+  const bool s_is_a = wave < 4;
+  const int s_row = 64 * (wave & 3) + lane;
+  const u32x4 rs = s_is_a
+      ? make_rsrc_words(As, (long long)nslab * a_ld * 4)
+      : make_rsrc_words(Bs + (size_t)seg * nslab * N * 4, (long long)nslab * N * 4);
+  const uint32_t s_base = s_is_a ? (uint32_t)(row0 + s_row) * 4 : (uint32_t)(n0 + s_row) * 4;
+  const uint32_t s_slab = s_is_a ? (uint32_t)a_ld * 4 : (uint32_t)N * 4;
+  const uint32_t s_lds = kMxDataBytes + (s_is_a ? 0u : 1024u) + (uint32_t)(wave & 3) * 256;
+
+  auto stage_addr = [&](int kt) {
+    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt & (kMxStages - 1)) * kMxStageBytes);
+  };
+  // load d (0, 1: A; 2, 3: B; 4: the scale word, even steps only) of step kt
+  auto dma = [&](uint32_t st, int d, int kt) {
+    const bool in_k = kt * kMxBK < Kd;
+    if (d < kMxDma) {
+      dma_load16(st + (8 * d + wave) * 1024,
+                 in_k ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
+    } else if (d < 2 * kMxDma) {
+      dma_load16(st + kMxBM * kMxBK + (8 * (d - kMxDma) + wave) * 1024,
+                 in_k ? d_off + (d - kMxDma) * d_stride + (uint32_t)kt * kMxBK : kOob, rb);
+    } else {
+      dma_load4(st + s_lds, in_k ? s_base + (uint32_t)(kt >> 1) * s_slab : kOob, rs);
+    }
+  };
+  auto issue_step = [&](int kt) {
+    const uint32_t st = stage_addr(kt);
+#pragma unroll
+    for (int d = 0; d < 2 * kMxDma; ++d) dma(st, d, kt);
+    if ((kt & 1) == 0) dma(st, 2 * kMxDma, kt);
+  };
+
+  // ---- LDS -> register fragment addresses (relative to a stage) ----
+  uint32_t a_rd[4][2], b_rd[2][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + rr;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) a_rd[i][c] = (uint32_t)r * kMxBK + (uint32_t)mx_swz(r, kh + 2 * c) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wn * 64 + j * 32 + rr;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      b_rd[j][c] = kMxBM * kMxBK + (uint32_t)r * kMxBK + (uint32_t)mx_swz(r, kh + 2 * c) * 16;
+  }
+  uint32_t sa_rd[4], sb_rd[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa_rd[i] = kMxDataBytes + (uint32_t)(wm * 128 + i * 32 + rr) * 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sb_rd[j] = kMxDataBytes + 1024 + (uint32_t)(wn * 64 + j * 32 + rr) * 4;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto read_a = [&](uint32_t st, int i) { return frag(lds_b128(st + a_rd[i][0]), lds_b128(st + a_rd[i][1])); };
+  auto read_b = [&](uint32_t st, int j) { return frag(lds_b128(st + b_rd[j][0]), lds_b128(st + b_rd[j][1])); };
+
+  // Software pipeline, one barrier per K-step, the step's eight MFMAs in two
+  // halves (tiles i = 0, 1, then i = 2, 3):
+  //   read a2, a3 of step kt                | half 0 of step kt
+  //   wait: step kt+1 landed; barrier
+  //   read a0, a1, b of step kt+1 (+ scale  | half 1 of step kt, refill of
+  //   words when kt+1 is even)              | step kt+3
+  // b of consecutive steps alternates between two register sets.  Scale words
+  // (4 A + 2 B per lane) cover a pair of steps; each step's bytes are
+  // extracted at its start.  Ring: step kt lives in slot kt % 4; iteration kt
+  // refills slot (kt-1) % 4, whose reads every wave finished before this
+  // iteration's barrier.  Loads younger than step kt+1 at the wait: step
+  // kt+2's four data loads, plus its scale word when kt+2 is even.
+  const int KT = Kd / kMxBK;
+  issue_step(0);
+  issue_step(1);
+  issue_step(2);
+  wait_vmcnt<9>();  // step 0 landed: younger are step 1 (4) and step 2 (4 + 1)
+  block_barrier();
+  i32x8 a01[2], a23[2], bs[2][2];
+  uint32_t wa[4], wb[2];
+  {
+    const uint32_t st = lds0;
+    a01[0] = read_a(st, 0);
+    a01[1] = read_a(st, 1);
+    bs[0][0] = read_b(st, 0);
+    bs[0][1] = read_b(st, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wa[i] = lds_b32(st + sa_rd[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wb[j] = lds_b32(st + sb_rd[j]);
+  }
+
+  auto step = [&](int kt, auto par) {
+    constexpr int P = decltype(par)::value;  // kt & 1
+    const uint32_t st = lds0 + (uint32_t)(kt & 3) * kMxStageBytes;
+    const uint32_t st1 = lds0 + (uint32_t)((kt + 1) & 3) * kMxStageBytes;
+    // this step's scale bytes: byte 2 (kt & 1) + kh of each word
+    int sa[4], sb[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = (int)((wa[i] >> (8 * (2 * P + kh))) & 0xffu);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sb[j] = (int)((wb[j] >> (8 * (2 * P + kh))) & 0xffu);
+    a23[0] = read_a(st, 2);
+    a23[1] = read_a(st, 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_mx8(bs[P][j], a01[i], acc[i][j], sb[j], sa[i]);
+    if (P == 0)
+      wait_vmcnt<5>();
+    else
+      wait_vmcnt<4>();
+    wait_lgkm0();
+    block_barrier();
+    // operands of step kt+1 (past the last step: harmless reads of a landed stage)
+    a01[0] = read_a(st1, 0);
+    a01[1] = read_a(st1, 1);
+    bs[P ^ 1][0] = read_b(st1, 0);
+    bs[P ^ 1][1] = read_b(st1, 1);
+    if (P == 1) {  // step kt+1 is even: the next pair's scale words
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wa[i] = lds_b32(st1 + sa_rd[i]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wb[j] = lds_b32(st1 + sb_rd[j]);
+    }
+    // half 1 with the refill of step kt+3 (past K: zeros into a slot never read)
+    const int kf = kt + 3;
+    const uint32_t stf = stage_addr(kf);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 2 + (t >> 1), j = t & 1;
+      acc[i][j] = mfma_mx8(bs[P][j], a23[i - 2], acc[i][j], sb[j], sa[i]);
+      dma(stf, t, kf);
+    }
+    if (P == 1) dma(stf, 2 * kMxDma, kf);  // kt + 3 even
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < KT) step(kt + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
+
+  // ---- epilogue: (GELU,) MX block maxima over lane pairs, E4M3 codes ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + i * 32 + rr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int nb = n0 + wn * 64 + j * 32;  // first column of this tile's block
+      float v[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        v[r] = EPI == kMxEpiGeluQuantOperand ? gelu_tanh_f32(acc[i][j][r]) : acc[i][j][r];
+        amax = fmaxf(amax, fabsf(v[r]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const uint32_t code = mx_scale_code(amax);
+      const float inv = mx_inv_scale(code);
+      uint32_t d[4];  // columns 8g + 4kh .. +3 of the block
+#pragma unroll
+      for (int g = 0; g < 4; ++g) d[g] = mx_encode4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], inv);
+      // lane pair exchange: lane kh = 0 stores columns 0-15, kh = 1 columns 16-31
+      const uint32_t x0 = __shfl_xor(kh ? d[0] : d[2], 32, kWave);
+      const uint32_t x1 = __shfl_xor(kh ? d[1] : d[3], 32, kWave);
+      const u32x4 o = kh ? u32x4{x0, d[2], x1, d[3]} : u32x4{d[0], x0, d[1], x1};
+      if (m < rows && nb < N) {
+        *(u32x4*)(C + (size_t)(row0 + m) * N + nb + 16 * kh) = o;
+        if (kh == 0) {
+          if (EPI == kMxEpiQuantRows)
+            Cs[(size_t)(row0 + m) * (N / kMxBlock) + nb / kMxBlock] = (uint8_t)code;
+          else
+            Cs[mx_operand_scale_index(c_ld, row0 + m, nb / kMxBlock)] = (uint8_t)code;
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
+  static bool lds_ok = false;
+  if (!lds_ok) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_mx8<EPI>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kMxSmem);
+    if (e != hipSuccess) return e;
+    lds_ok = true;
+  }
+  if (a.Kd <= 0 || a.Kd % kMxBK != 0 || a.N <= 0 || a.N % kMxBlock != 0) return hipErrorInvalidValue;
+  const int ntc = (a.N + kMxBN - 1) / kMxBN;
+  const int mtb = a.offsets ? (a.max_rows + kMxBM - 1) / kMxBM + a.G
+                            : (a.fixed_rows + kMxBM - 1) / kMxBM;
+  const long long grid = (long long)mtb * ntc;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  k_grouped_gemm_mx8<EPI><<<(unsigned)grid, kMxThreads, kMxSmem, st>>>(
+      a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
+      a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_mx8(const MxGemmArgs& a, hipStream_t st) {
+  switch (a.epi) {
+    case kMxEpiQuantRows: return launch_mx8<kMxEpiQuantRows>(a, st);
+    case kMxEpiGeluQuantOperand: return launch_mx8<kMxEpiGeluQuantOperand>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -55,6 +55,31 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
+// The dispatch copy in MXFP8: bf16 token rows quantised on the way (mx.h),
+// codes [max_rows][H] and operand-layout scales (leading dimension xp_ld);
+// optionally also every token's own row (x_q [T][H], scales with ld T).
+struct PermuteMx8Args {
+  const void* x;       // bf16 [T][H]
+  const int32_t* topk_ids;
+  const int32_t* hist;
+  const int32_t* lrank;
+  int32_t* base;
+  int32_t* counts;
+  int32_t* kept;
+  int32_t* offsets;
+  int32_t* row_of;
+  int32_t* token_of;
+  int32_t* n_dropped;
+  uint8_t* xp_q;
+  uint8_t* xp_s;
+  int xp_ld;
+  uint8_t* x_q;        // nullable
+  uint8_t* x_s;
+  int T, H, E, K;
+  int C;
+};
+hipError_t launch_permute_mx8(const PermuteMx8Args& a, hipStream_t st);
+
 // Operand layouts of the grouped GEMM (the contraction runs over K):
 //   kGemmNN: A [rows][Kd], B [G][Kd][N] -> C [rows][N]; rows segmented by offsets
 //   kGemmNT: A [rows][Kd], B [G][N][Kd] -> C [rows][N]; rows segmented by offsets
@@ -84,6 +109,32 @@ struct GemmArgs {
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& a, hipStream_t st);
 
+// MXFP8 grouped GEMM (mx.h for the formats):
+//   A [a_rows][Kd] codes + As (operand layout, leading dimension a_ld),
+//   B [G][N][Kd] codes + Bs [G][ceil(Kd/128)][N][4],
+//   C [rows][N] codes + Cs: row layout [rows][N/32] (kMxEpiQuantRows) or
+//   operand layout with leading dimension c_ld (kMxEpiGeluQuantOperand).
+// Kd is a multiple of 64, N of 32.
+enum MxEpi { kMxEpiQuantRows = 0, kMxEpiGeluQuantOperand = 1 };
+struct MxGemmArgs {
+  int epi = kMxEpiQuantRows;
+  const uint8_t* A = nullptr;
+  const uint8_t* As = nullptr;
+  int a_ld = 0;
+  const uint8_t* B = nullptr;
+  const uint8_t* Bs = nullptr;
+  uint8_t* C = nullptr;
+  uint8_t* Cs = nullptr;
+  int c_ld = 0;
+  const int32_t* offsets = nullptr;  // [G+1] device, or nullptr: one segment of fixed_rows rows
+  int G = 1;
+  int fixed_rows = 0;
+  int max_rows = 0;
+  int Kd = 0;
+  int N = 0;
+};
+hipError_t launch_grouped_gemm_mx8(const MxGemmArgs& a, hipStream_t st);
+
 struct CombineArgs {
   bool bf16;
   const void* out;
@@ -94,6 +145,26 @@ struct CombineArgs {
   int T, H, K;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// MXFP8 combine: out_q [rows][H] codes with row-layout scales [rows][H/32];
+// sh_q / sh_s the same for the shared expert's [T][H] output (nullable);
+// y bf16 [T][H].
+struct CombineMx8Args {
+  const uint8_t* out_q;
+  const uint8_t* out_s;
+  const int32_t* row_of;
+  const float* topk_w;
+  const uint8_t* sh_q;
+  const uint8_t* sh_s;
+  void* y;
+  int T, H, K;
+};
+hipError_t launch_combine_mx8(const CombineMx8Args& a, hipStream_t st);
+
+// w [G][Kd][N] (bf16 or fp32) -> codes [G][N][Kd] + operand-layout scales
+// [G][ceil(Kd/128)][N][4] (blocks along Kd).
+hipError_t launch_quantize_weight_mx8(const void* w, bool bf16_in, int G, int Kd, int N,
+                                      uint8_t* q, uint8_t* s, hipStream_t st);
 
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int T, int E, int K,
                       int nblk, hipStream_t st);

@@ -15,6 +15,7 @@
 // map is bit-exact and deterministic, with no atomics.
 #include "common.h"
 #include "kernels.h"
+#include "mx.h"
 
 namespace moe {
 
@@ -73,24 +74,17 @@ __device__ __forceinline__ void segment_offsets(const int32_t* __restrict__ coun
   total = __shfl(incl, 63, kWave);
 }
 
-// One wave per token: its row map entries, then the copy of its row to each
-// kept destination.  The row is read from HBM once (16-byte vectors, VPL per
-// lane per chunk, all loads of a chunk issued before its stores).  The wave
-// of token 0 also publishes kept, offsets and n_dropped.
-template <int VPL>
-__global__ __launch_bounds__(256) void k_permute(
-    const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int E, int K, int C,
-    int nblk) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // wave-uniform; the kernel has no barrier (token 0 always runs)
+// The row map of token t, computed by its wave: lane k < K returns the packed
+// row of assignment (t, k) (-1 when dropped) and writes row_of / token_of;
+// other lanes return -1.  The wave of token 0 also publishes kept, offsets
+// and n_dropped.  Index loads come first (the counts load independently of
+// ids and lrank, so two dependent round trips precede any row traffic).
+__device__ __forceinline__ int permute_row_map(
+    int t, const int32_t* __restrict__ ids, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of, int E, int K, int C, int nblk) {
   const int lane = threadIdx.x & 63;
-  // row-map work first (the counts load independently of ids and lrank, so
-  // two dependent round trips precede the copy); the row loads come after,
-  // since vmcnt waits are in issue order
   int e = 0, lr = 0;
   if (lane < K) {
     e = ids[(size_t)t * K + lane];
@@ -114,18 +108,36 @@ __global__ __launch_bounds__(256) void k_permute(
     }
   }
   int row = -1;
-  {
-    // offsets[e] lives in lane e/4, slot e%4 (all lanes take part in the shuffles)
-    const int o0 = __shfl(off4[0], e >> 2, kWave), o1 = __shfl(off4[1], e >> 2, kWave);
-    const int o2 = __shfl(off4[2], e >> 2, kWave), o3 = __shfl(off4[3], e >> 2, kWave);
-    const int oe = (e & 3) == 0 ? o0 : (e & 3) == 1 ? o1 : (e & 3) == 2 ? o2 : o3;
-    if (lane < K) {
-      const int r = base[(size_t)e * nblk + t / kRouteBlock] + lr;
-      row = r < C ? oe + r : -1;
-      row_of[(size_t)t * K + lane] = row;
-      if (row >= 0) token_of[row] = t;
-    }
+  // offsets[e] lives in lane e/4, slot e%4 (all lanes take part in the shuffles)
+  const int o0 = __shfl(off4[0], e >> 2, kWave), o1 = __shfl(off4[1], e >> 2, kWave);
+  const int o2 = __shfl(off4[2], e >> 2, kWave), o3 = __shfl(off4[3], e >> 2, kWave);
+  const int oe = (e & 3) == 0 ? o0 : (e & 3) == 1 ? o1 : (e & 3) == 2 ? o2 : o3;
+  if (lane < K) {
+    const int r = base[(size_t)e * nblk + t / kRouteBlock] + lr;
+    row = r < C ? oe + r : -1;
+    row_of[(size_t)t * K + lane] = row;
+    if (row >= 0) token_of[row] = t;
   }
+  return row;
+}
+
+// One wave per token: its row map entries, then the copy of its row to each
+// kept destination.  The row is read from HBM once (16-byte vectors, VPL per
+// lane per chunk, all loads of a chunk issued before its stores; vmcnt waits
+// are in issue order, so the row loads come after the index loads).
+template <int VPL>
+__global__ __launch_bounds__(256) void k_permute(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int E, int K, int C,
+    int nblk) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; the kernel has no barrier (token 0 always runs)
+  const int lane = threadIdx.x & 63;
+  const int row = permute_row_map(t, ids, lrank, base, counts, kept, offsets, n_dropped, row_of,
+                                  token_of, E, K, C, nblk);
   const u32x4* src = x + (size_t)t * nvec;
   u32x4 v[VPL];
   int rows[8];
@@ -151,6 +163,83 @@ __global__ __launch_bounds__(256) void k_permute(
   }
 }
 
+// The same row map, with the copy quantising each bf16 token row to MXFP8
+// (mx.h) on the way: lane l of chunk j holds 8 values (16 bytes), four
+// consecutive lanes one block of 32.  The block maximum is a max over the
+// lane quad; each destination gets 8 code bytes per lane and, from the first
+// lane of every 16, one 4-byte word of four block scales (operand layout,
+// leading dimension xp_ld).  With x_q set the token's own quantised row is
+// also written (row t, leading dimension T), for the shared expert.
+template <int VPL>
+__global__ __launch_bounds__(256) void k_permute_mx8(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ token_of, u32x2* __restrict__ xp_q, uint8_t* __restrict__ xp_s,
+    int xp_ld, u32x2* __restrict__ x_q, uint8_t* __restrict__ x_s, int T, int nvec, int E,
+    int K, int C, int nblk) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; no barrier in this kernel
+  const int lane = threadIdx.x & 63;
+  const int row = permute_row_map(t, ids, lrank, base, counts, kept, offsets, n_dropped, row_of,
+                                  token_of, E, K, C, nblk);
+  const u32x4* src = x + (size_t)t * nvec;
+  int rows[9];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rows[k] = k < K ? __shfl(row, k, kWave) : -1;
+  rows[8] = x_q ? t : -1;  // the shared expert's copy
+  for (int c0 = 0; c0 < nvec; c0 += 64 * VPL) {
+    u32x4 v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int c = c0 + lane + 64 * j;
+      v[j] = c < nvec ? src[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x2 q[VPL];
+    uint32_t sw[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(v[j][i] & 0xffffu);
+        f[2 * i + 1] = bf16_bits_to_f32(v[j][i] >> 16);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+      const uint32_t code = mx_scale_code(amax);
+      const float inv = mx_inv_scale(code);
+      q[j] = u32x2{mx_encode4(f[0], f[1], f[2], f[3], inv), mx_encode4(f[4], f[5], f[6], f[7], inv)};
+      // scale word of the 16-lane group (blocks of lanes +0, +4, +8, +12)
+      const uint32_t c4 = __shfl_down(code, 4, kWave), c8 = __shfl_down(code, 8, kWave);
+      const uint32_t c12 = __shfl_down(code, 12, kWave);
+      sw[j] = code | (c4 << 8) | (c8 << 16) | (c12 << 24);
+    }
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      if (rows[k] >= 0) {
+        const int r = rows[k];
+        u32x2* dq = k < 8 ? xp_q : x_q;
+        uint8_t* ds = k < 8 ? xp_s : x_s;
+        const int ld = k < 8 ? xp_ld : T;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = c0 + lane + 64 * j;  // 16-byte input chunk = 8 values
+          if (c < nvec) {
+            dq[(size_t)r * nvec + c] = q[j];
+            if ((lane & 15) == 0)
+              *(uint32_t*)(ds + ((size_t)(c >> 4) * ld + r) * 4) = sw[j];
+          }
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int nblk = (a.T + kRouteBlock - 1) / kRouteBlock;
   k_scan_blocks<<<a.E, 256, 0, st>>>(a.hist, a.base, a.counts, nblk);
@@ -160,6 +249,18 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   k_permute<8><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.counts,
                                      a.kept, a.offsets, a.n_dropped, a.row_of, a.token_of,
                                      (u32x4*)a.xp, a.T, nvec, a.E, a.K, a.C, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_mx8(const PermuteMx8Args& a, hipStream_t st) {
+  const int nblk = (a.T + kRouteBlock - 1) / kRouteBlock;
+  k_scan_blocks<<<a.E, 256, 0, st>>>(a.hist, a.base, a.counts, nblk);
+  const int nvec = a.H / 8;  // 16-byte bf16 chunks per row
+  const int grid = (a.T + 3) / 4;
+  k_permute_mx8<4><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base,
+                                         a.counts, a.kept, a.offsets, a.n_dropped, a.row_of,
+                                         a.token_of, (u32x2*)a.xp_q, a.xp_s, a.xp_ld,
+                                         (u32x2*)a.x_q, a.x_s, a.T, nvec, a.E, a.K, a.C, nblk);
   return hipGetLastError();
 }
 

@@ -184,3 +184,139 @@ def backward(buf: MoeBuffers, g: GradBuffers, p: dict, dy, alpha: float = 0.0,
     expert_ffn_backward(buf, g, p, dy, stream)
     permute_backward(buf, g, p, stream)
     return g
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 forward (moe_*_mxfp8): FP8 dispatch, expert GEMMs and combine
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class MxWeights:
+    """Expert weights in MXFP8 (moe_quantize_weights_mxfp8): codes [E,N,K]
+    with K the contraction dimension, operand-layout scales."""
+    w1_q: torch.Tensor
+    w1_s: torch.Tensor
+    w2_q: torch.Tensor
+    w2_s: torch.Tensor
+    ws1_q: Optional[torch.Tensor]
+    ws1_s: Optional[torch.Tensor]
+    ws2_q: Optional[torch.Tensor]
+    ws2_s: Optional[torch.Tensor]
+
+    @staticmethod
+    def quantize(w: Workload, p: dict, stream=None) -> "MxWeights":
+        dev = p["w1"].device
+        dt = B.MOE_BF16 if p["w1"].dtype == torch.bfloat16 else B.MOE_F32
+
+        def q(t, G, K, N):
+            codes = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((G * B.moe_mx_operand_scale_bytes(N, K),), dtype=torch.uint8,
+                             device=dev)
+            B.moe_quantize_weights_mxfp8(t, dt, G, K, N, codes, sc, stream)
+            return codes, sc
+
+        w1_q, w1_s = q(p["w1"], w.E, w.H, w.h)
+        w2_q, w2_s = q(p["w2"], w.E, w.h, w.H)
+        ws1_q = ws1_s = ws2_q = ws2_s = None
+        if w.hs:
+            ws1_q, ws1_s = q(p["ws1"], 1, w.H, w.hs)
+            ws2_q, ws2_s = q(p["ws2"], 1, w.hs, w.H)
+        return MxWeights(w1_q, w1_s, w2_q, w2_s, ws1_q, ws1_s, ws2_q, ws2_s)
+
+
+@dataclasses.dataclass
+class MxBuffers:
+    """Buffers of one MXFP8 forward: the routing outputs of :class:`MoeBuffers`
+    and FP8 codes + scales in place of the bf16 intermediates."""
+    shape: B.moe_shape
+    logits: torch.Tensor
+    topk_ids: torch.Tensor
+    topk_w: torch.Tensor
+    aux: torch.Tensor
+    counts: torch.Tensor
+    kept: torch.Tensor
+    offsets: torch.Tensor
+    row_of: torch.Tensor
+    token_of: torch.Tensor
+    n_dropped: torch.Tensor
+    xp_q: torch.Tensor
+    xp_s: torch.Tensor
+    x_q: Optional[torch.Tensor]
+    x_s: Optional[torch.Tensor]
+    h_q: torch.Tensor
+    h_s: torch.Tensor
+    out_q: torch.Tensor
+    out_s: torch.Tensor
+    hsh_q: Optional[torch.Tensor]
+    hsh_s: Optional[torch.Tensor]
+    sh_q: Optional[torch.Tensor]
+    sh_s: Optional[torch.Tensor]
+    y: torch.Tensor
+    ws: torch.Tensor
+
+    @staticmethod
+    def allocate(w: Workload, device="cuda") -> "MxBuffers":
+        s = shape_of(w)
+        st = B.moe_check_shape(s)
+        if st != B.MOE_OK:
+            raise B.MoeError("moe_check_shape", st, B.moe_status_string(st))
+        n = max(B.moe_max_rows(s), 1)
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        u8 = dict(dtype=torch.uint8, device=device)
+        opsc = lambda R, K: torch.empty((B.moe_mx_operand_scale_bytes(R, K),), **u8)
+        return MxBuffers(
+            shape=s,
+            logits=torch.empty((w.T, w.E), **f32),
+            topk_ids=torch.empty((w.T, w.K), **i32),
+            topk_w=torch.empty((w.T, w.K), **f32),
+            aux=torch.empty((1,), **f32),
+            counts=torch.empty((w.E,), **i32),
+            kept=torch.empty((w.E,), **i32),
+            offsets=torch.empty((w.E + 1,), **i32),
+            row_of=torch.empty((w.T, w.K), **i32),
+            token_of=torch.empty((n,), **i32),
+            n_dropped=torch.empty((1,), **i32),
+            xp_q=torch.empty((n, w.H), **u8),
+            xp_s=opsc(n, w.H),
+            x_q=torch.empty((w.T, w.H), **u8) if w.hs else None,
+            x_s=opsc(w.T, w.H) if w.hs else None,
+            h_q=torch.empty((n, w.h), **u8),
+            h_s=opsc(n, w.h),
+            out_q=torch.empty((n, w.H), **u8),
+            out_s=torch.empty((n, w.H // 32), **u8),
+            hsh_q=torch.empty((w.T, w.hs), **u8) if w.hs else None,
+            hsh_s=opsc(w.T, w.hs) if w.hs else None,
+            sh_q=torch.empty((w.T, w.H), **u8) if w.hs else None,
+            sh_s=torch.empty((w.T, w.H // 32), **u8) if w.hs else None,
+            y=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=device),
+            ws=torch.empty((B.moe_workspace_size(s),), **u8),
+        )
+
+
+def permute_mxfp8(buf: MxBuffers, p: dict, stream=None):
+    B.moe_permute_mxfp8(buf.shape, p["x"], buf.topk_ids, buf.ws, buf.counts, buf.kept,
+                        buf.offsets, buf.row_of, buf.token_of, buf.n_dropped, buf.xp_q,
+                        buf.xp_s, buf.x_q, buf.x_s, stream)
+
+
+def expert_ffn_mxfp8(buf: MxBuffers, mw: MxWeights, stream=None):
+    B.moe_expert_ffn_mxfp8(buf.shape, buf.xp_q, buf.xp_s, buf.offsets, mw.w1_q, mw.w1_s,
+                           mw.w2_q, mw.w2_s, buf.h_q, buf.h_s, buf.out_q, buf.out_s, buf.x_q,
+                           buf.x_s, mw.ws1_q, mw.ws1_s, mw.ws2_q, mw.ws2_s, buf.hsh_q,
+                           buf.hsh_s, buf.sh_q, buf.sh_s, stream)
+
+
+def combine_mxfp8(buf: MxBuffers, stream=None):
+    B.moe_combine_mxfp8(buf.shape, buf.out_q, buf.out_s, buf.row_of, buf.topk_w, buf.sh_q,
+                        buf.sh_s, buf.y, stream)
+
+
+def forward_mxfp8(buf: MxBuffers, p: dict, mw: MxWeights, stream=None) -> MxBuffers:
+    """route -> aux_loss -> permute_mxfp8 -> expert_ffn_mxfp8 -> combine_mxfp8."""
+    route(buf, p, stream)
+    aux_loss(buf, stream)
+    permute_mxfp8(buf, p, stream)
+    expert_ffn_mxfp8(buf, mw, stream)
+    combine_mxfp8(buf, stream)
+    return buf

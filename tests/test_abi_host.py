@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -183,3 +183,41 @@ def test_backward_calls_reject_bad_arguments_before_launch(lib):
                                     None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_permute_backward(ctypes.byref(s), p, p, None, p, p, p, p, 8,
                                     None) == B.MOE_ERR_WORKSPACE
+
+
+def test_mxfp8_calls_reject_bad_arguments_before_launch(lib):
+    """The FP8 path needs bf16, hidden sizes in whole 64-value K-steps and no
+    training flag; null or misaligned pointers are refused."""
+    p = 0x4000
+    big = 1 << 30
+    ok = shape(H=128, h_exp=256)
+    perm = lambda sh, xp_q=p, x=p: (ctypes.byref(sh), x, p, p, big, p, p, p, p, p, p, xp_q, p,
+                                    None, None, None)
+    assert lib.moe_permute_mxfp8(*perm(shape(H=128, h_exp=256, dtype=B.MOE_F32))) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_mxfp8(*perm(shape(H=96, h_exp=256))) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_mxfp8(*perm(shape(H=128, h_exp=256, flags=B.MOE_FLAG_TRAIN))) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute_mxfp8(*perm(ok, xp_q=None)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_mxfp8(*perm(ok, x=p + 8)) == B.MOE_ERR_INVALID_ARG
+    # a shared expert needs the quantised-x outputs
+    assert lib.moe_permute_mxfp8(*perm(shape(H=128, h_exp=256, h_shared=64))) == \
+        B.MOE_ERR_INVALID_ARG
+    ffn = lambda sh, h_q=p: (ctypes.byref(sh), p, p, p, p, p, p, p, h_q, p, p, p) + \
+        (None,) * 10 + (None,)
+    assert lib.moe_expert_ffn_mxfp8(*ffn(shape(H=128, h_exp=200))) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_mxfp8(*ffn(ok, h_q=None)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_mxfp8(*ffn(ok, h_q=p + 4)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_mxfp8(*ffn(shape(H=128, h_exp=256, h_shared=64))) == \
+        B.MOE_ERR_INVALID_ARG
+    comb = lambda sh, y=p: (ctypes.byref(sh), p, p, p, p, None, None, y, None)
+    assert lib.moe_combine_mxfp8(*comb(ok, y=None)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_mxfp8(*comb(shape(H=128, h_exp=256, dtype=B.MOE_F32))) == \
+        B.MOE_ERR_UNSUPPORTED
+    q = lambda K, N, dt=B.MOE_BF16, w=p: (w, dt, 2, K, N, p, p, None)
+    assert lib.moe_quantize_weights_mxfp8(*q(96, 64)) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_weights_mxfp8(*q(128, 48)) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_weights_mxfp8(*q(128, 64, dt=7)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_weights_mxfp8(*q(128, 64, w=None)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_operand_scale_bytes(100, 192) == 2 * 100 * 4
+    assert lib.moe_mx_operand_scale_bytes(7, 128) == 7 * 4

@@ -1,0 +1,332 @@
+"""GPU parity of the MXFP8 forward against the MXFP8 oracle, through the C ABI.
+
+Protocol:
+  1. seeded inputs feed both sides; the GPU runs route -> aux_loss ->
+     permute_mxfp8 -> expert_ffn_mxfp8 -> combine_mxfp8 with weights from
+     moe_quantize_weights_mxfp8;
+  2. routing is checked bit-exactly as in the bf16 tests (oracle routing from
+     the GPU's fp32 logits);
+  3. byte work is bit-exact: the quantised weights, the quantised dispatched
+     rows (codes and scales) and the shared expert's quantised x;
+  4. the FP8 results of the GEMMs (h, out, and the shared expert's) are
+     quantised by both sides from float32 values that differ by accumulation
+     order (and by the MFMA's internal precision), so a value near a rounding
+     boundary may land on the neighbouring code.  h differs only by such
+     decisions: at least 99% of its dequantised values equal and every one
+     within one E4M3 step (plus 2^X of its block).  An output row then sums
+     those h values: each neighbouring-code h_j moves output n by up to an
+     eighth of |h_j W2[j, n]|, and with h_exp = 14336 a row carries about a
+     dozen of them, so a few percent of outputs land on the neighbouring code
+     too.  Required for out: at least 90% equal (a wrong rounding rule would
+     move about half) and every value within one step plus 16 * 2^X (a
+     sixteenth to a thirty-second of its block's maximum);
+  5. y (bf16): every element within the sum over its kept slots of
+     |w| times that output bound, plus one bf16 rounding; relative Frobenius
+     error <= 1e-2.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_08_amd import binding as B
+from mixture_experts_layer_08_amd import layer
+from mixture_experts_layer_08_amd.inputs import WORKLOADS, Workload, make_inputs, sample_tokens
+from oracle import moe_oracle as O
+from oracle import mxfp8_oracle as M
+from tests.test_gpu_parity import check_routing
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np32(t):
+    return None if t is None else t.detach().to("cpu").to(torch.float32).numpy()
+
+
+def u8(t):
+    return t.detach().cpu().numpy()
+
+
+def op_rows(flat, R, Kd):
+    """Operand-layout scales [ceil(Kd/128)][R][4] -> row layout [R][Kd/32]."""
+    ns = (Kd + 127) // 128
+    a = u8(flat)[: ns * R * 4].reshape(ns, R, 4).transpose(1, 0, 2).reshape(R, ns * 4)
+    return a[:, : Kd // 32]
+
+
+def run_mx(w: Workload, p: dict):
+    mw = layer.MxWeights.quantize(w, p)
+    buf = layer.MxBuffers.allocate(w)
+    layer.forward_mxfp8(buf, p, mw)
+    torch.cuda.synchronize()
+    return buf, mw
+
+
+def oracle_mx(w: Workload, p: dict, buf):
+    l = buf.logits.cpu().numpy().astype(np.float64)
+    return M.forward_mxfp8(np32(p["x"]), np32(p["w_r"]), None, np32(p["w1"]), np32(p["w2"]),
+                           np32(p["ws1"]), np32(p["ws2"]), K=w.K, cf=w.cf, logits=l)
+
+
+def step_of(codes, scales_rows):
+    """E4M3 spacing at each element times its block's 2^X (the step to the
+    next larger magnitude; 32 * 2^X at 448)."""
+    c = codes.astype(np.int64) & 0x7F
+    pos = M.e4m3_value(np.arange(0x7F))
+    nxt = np.where(c < 0x7E, pos[np.minimum(c + 1, 0x7E)] - pos[np.minimum(c, 0x7E)], 32.0)
+    X = np.repeat(scales_rows.astype(np.int64) - 127, 32, axis=1)
+    return nxt * np.exp2(X), np.exp2(X)
+
+
+def check_mx_close(name, gc, gs, rc, rs, min_exact=0.99, units=1.0):
+    """Dequantised GPU vs oracle MXFP8 tensors (codes [R][C], row-layout
+    scales): each value within one step plus ``units`` * 2^X of its block."""
+    a = M.mx_dequantize(gc, gs, axis=1)
+    b = M.mx_dequantize(rc, rs, axis=1)
+    sa, ua = step_of(gc, gs)
+    sb, ub = step_of(rc, rs)
+    tol = np.maximum(sa, sb) + units * np.maximum(ua, ub)
+    d = np.abs(a - b)
+    exact = float(np.mean(d == 0)) if d.size else 1.0
+    worst = float(np.max(d / tol)) if d.size else 0.0
+    say(f"  {name}: {d.size} values, {exact:.5%} equal, scales equal {np.mean(gs == rs):.5%}, "
+        f"worst |diff| / tol {worst:.3f}")
+    assert exact >= min_exact, f"{name}: only {exact:.4%} equal"
+    assert worst <= 1.0, f"{name}: a value off by more than the bound"
+    return tol
+
+
+def check_forward(w: Workload, p: dict, buf, mw, ref=None):
+    r = check_routing(w, buf)
+    ref = ref if ref is not None else oracle_mx(w, p, buf)
+    N = int(buf.offsets[-1].item())
+    nmax = buf.xp_q.shape[0]
+    tok = r["token_of"]
+    # byte work: bit-exact
+    assert np.array_equal(u8(buf.xp_q[:N]), ref["x_codes"][tok]), "dispatched codes differ"
+    assert np.array_equal(op_rows(buf.xp_s, nmax, w.H)[:N], ref["x_scales"][tok]), \
+        "dispatched scales differ"
+    if w.hs:
+        assert np.array_equal(u8(buf.x_q), ref["x_codes"]), "shared-expert x codes differ"
+        assert np.array_equal(op_rows(buf.x_s, w.T, w.H), ref["x_scales"])
+    # GEMM results: neighbouring codes allowed at rounding boundaries
+    check_mx_close("h", u8(buf.h_q[:N]), op_rows(buf.h_s, nmax, w.h)[:N], ref["h_codes"],
+                   ref["h_scales"])
+    tol_out = check_mx_close("out", u8(buf.out_q[:N]), u8(buf.out_s[:N]), ref["o_codes"],
+                             ref["o_scales"], min_exact=0.9, units=16.0)
+    tol_sh = None
+    if w.hs:
+        check_mx_close("shared h", u8(buf.hsh_q), op_rows(buf.hsh_s, w.T, w.hs),
+                       ref["sh_h_codes"], ref["sh_h_scales"])
+        tol_sh = check_mx_close("shared out", u8(buf.sh_q), u8(buf.sh_s), ref["sh_codes"],
+                                ref["sh_scales"], min_exact=0.9, units=16.0)
+    got = buf.y.cpu().to(torch.float64).numpy()
+    want = ref["y"]
+    bound = np.zeros_like(want)
+    ro, wt = r["row_of"], r["w"]
+    for k in range(w.K):
+        m = ro[:, k] >= 0
+        bound[m] += np.abs(wt[m, k])[:, None] * tol_out[ro[m, k]]
+    if tol_sh is not None:
+        bound += tol_sh
+    bound += 2.0 ** -8 * np.abs(want) + 1e-30  # bf16 rounding of y
+    worst = float(np.max(np.abs(got - want) / bound))
+    err = float(np.abs(got - want).max()) / max(float(np.abs(want).max()), 1e-30)
+    fro = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    say(f"  y: worst |diff| / bound {worst:.3f}, max rel err {err:.3e}, relative Frobenius "
+        f"error {fro:.3e} (tol 1e-2)")
+    assert worst <= 1.0
+    assert fro <= 1e-2
+    return r, ref
+
+
+# ---------------------------------------------------------------- byte work
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G,K,N", [(3, 192, 96), (1, 64, 32), (2, 4096, 64)])
+def test_quantize_weights_bit_exact(dtype, G, K, N):
+    """Per-column magnitudes from 2^-30 to 2^30, a zero column, exact E4M3
+    values at the top of the range, and ties: codes and scales bit-exact."""
+    say(f"[quantize weights {dtype}] G={G} K={K} N={N}")
+    g = torch.Generator().manual_seed(G * 1000 + K + N)
+    w = torch.randn((G, K, N), generator=g) * torch.exp2(torch.randint(-30, 31, (G, 1, N),
+                                                                       generator=g).float())
+    w[:, :, 0] = 0.0
+    w[0, :32, 1] = 448.0 * 2.0 ** -5
+    w[0, 32:64, 1] = torch.tensor([1.0, 1.0625, 1.125, 1.1875] * 8)  # 1.0625: a tie
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    w = w.to(tdt)
+    dev = w.to("cuda")
+    q = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((G * B.moe_mx_operand_scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_weights_mxfp8(dev, B.MOE_BF16 if dtype == "bf16" else B.MOE_F32, G, K, N, q, s)
+    torch.cuda.synchronize()
+    rc, rs = M.quantize_weights(w.to(torch.float32).numpy())
+    assert np.array_equal(u8(q), rc.transpose(0, 2, 1))
+    per = B.moe_mx_operand_scale_bytes(N, K)
+    for e in range(G):
+        assert np.array_equal(op_rows(s[e * per:(e + 1) * per], N, K), rs[e].T), f"scales {e}"
+
+
+def test_dispatch_codes_bit_exact_and_extreme_rows():
+    """Rows of zeros, rows scaled by 2^-40 .. 2^40, values that saturate: the
+    dispatched codes and scales equal the oracle's quantisation of x."""
+    w = Workload("extreme", T=300, H=192, E=5, K=2, h=64, hs=64, cf=1.0)
+    say(f"[dispatch] {w}")
+    p = make_inputs(w, seed=21, device="cuda")
+    x = p["x"].float()
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x *= torch.exp2(torch.randint(-40, 41, (w.T, 1), generator=g, device="cuda").float())
+    x[7] = 0.0
+    x[8, :32] = torch.tensor([480.0] + [1.0] * 31, device="cuda")  # 480 / 2^0 saturates
+    p["x"] = x.to(torch.bfloat16)
+    buf, mw = run_mx(w, p)
+    check_forward(w, p, buf, mw)
+
+
+# ---------------------------------------------------------------- whole forward
+
+CASES = [
+    ("tiny", dict(T=256, H=64, E=4, K=2, h=128, cf=0.0)),
+    ("ragged_odd_ksteps", dict(T=333, H=192, E=6, K=3, h=320, hs=128, cf=0.9, bias="normal")),
+    ("one_expert", dict(T=1000, H=128, E=1, K=1, h=64, cf=0.0)),
+    ("wide_h_tail", dict(T=130, H=256, E=2, K=1, h=576, cf=0.0)),
+    ("T1", dict(T=1, H=64, E=4, K=2, h=64, cf=1.25)),
+    ("E256_K8", dict(T=130, H=64, E=256, K=8, h=64, cf=1.25)),
+    ("C1_drops", dict(T=257, H=64, E=8, K=2, h=64, cf=0.01)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_forward_parity(name, kw):
+    w = Workload(name, **kw)
+    say(f"[mxfp8 {name}] {w}")
+    p = make_inputs(w, seed=13, device="cuda")
+    buf, mw = run_mx(w, p)
+    check_forward(w, p, buf, mw)
+
+
+def test_small_bf16_full_tensors():
+    w = WORKLOADS["small_bf16"]
+    say(f"[mxfp8 small_bf16] {w}")
+    p = make_inputs(w, seed=0, device="cuda")
+    buf, mw = run_mx(w, p)
+    _, ref = check_forward(w, p, buf, mw)
+    # distance from the bf16 layer (information: the cost of FP8)
+    f = O.forward_tokens(np32(p["x"]), np32(p["w1"]), np32(p["w2"]), None, None,
+                         O.route(buf.logits.cpu().numpy().astype(np.float64), w.E, w.K, w.cf),
+                         np.arange(0, w.T, 16))
+    d = np.linalg.norm(ref["y"][::16] - f) / np.linalg.norm(f)
+    say(f"  FP8 layer vs float layer: relative Frobenius difference {d:.4f}")
+
+
+def test_empty_experts_and_all_dropped_tokens():
+    w = Workload("empty", T=400, H=64, E=8, K=2, h=64, cf=0.5)
+    p = make_inputs(w, seed=3, device="cuda")
+    p["b_r"] = torch.zeros(8, device="cuda")
+    p["b_r"][:2] = 100.0
+    buf, mw = run_mx(w, p)
+    r, _ = check_forward(w, p, buf, mw)
+    assert (r["kept"][2:] == 0).all() and (r["row_of"] < 0).all(1).sum() > 0
+
+
+def test_determinism_bitwise():
+    w = WORKLOADS["small_bf16"].replace(T=1000, cf=0.9)
+    p = make_inputs(w, seed=5, device="cuda")
+    a, _ = run_mx(w, p)
+    b, _ = run_mx(w, p)
+    for name in ("xp_q", "xp_s", "h_q", "h_s", "out_q", "out_s"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
+
+
+# ---------------------------------------------------------------- full size
+
+def test_mixtral_full_size_sampled():
+    """T=32768, H=4096, E=8, top-2, h=14336 in the bench's launch
+    configuration.  Routing complete and bit-exact; dispatched codes of a
+    token sample bit-exact; weight codes of sampled columns bit-exact; 16
+    packed rows of each of two experts against the oracle's FP8 expert FFN
+    (all h columns, four 32-column blocks of out); y of sampled tokens
+    against combine's definition on the GPU's out rows (a property that holds
+    at any size)."""
+    w = WORKLOADS["mixtral_bf16"]
+    say(f"[mxfp8 mixtral full size] {w}")
+    p = make_inputs(w, seed=0, device="cuda")
+    buf, mw = run_mx(w, p)
+    r = check_routing(w, buf)
+    N = int(buf.offsets[-1].item())
+    nmax = buf.xp_q.shape[0]
+    toks = sample_tokens(w.T, 256, seed=9).numpy()
+    xs = np32(p["x"][torch.as_tensor(toks, device="cuda")])
+    xc, xsc = M.mx_quantize(xs, axis=1)
+    ro = r["row_of"]
+    xps = op_rows(buf.xp_s, nmax, w.H)
+    for i, t in enumerate(toks):
+        for k in range(w.K):
+            if ro[t, k] >= 0:
+                assert np.array_equal(u8(buf.xp_q[int(ro[t, k])]), xc[i]), (t, k)
+                assert np.array_equal(xps[int(ro[t, k])], xsc[i]), (t, k)
+    say("  dispatched codes of 256 tokens bit-exact")
+    cols = np.array([0, 1, 5000, 14335])
+    w1c = np32(p["w1"][:, :, torch.as_tensor(cols, device="cuda")])
+    rc, rs = M.quantize_weights(w1c)
+    gq = u8(mw.w1_q[:, torch.as_tensor(cols, device="cuda"), :])
+    assert np.array_equal(gq, rc.transpose(0, 2, 1))
+    say("  W1 codes of sampled columns bit-exact")
+    off = r["offsets"]
+    blocks = np.array([0, 37, 64, 127])  # 32-column blocks of out
+    ocols = (blocks[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    for e in (0, 5):
+        if off[e + 1] <= off[e]:
+            continue
+        rows = np.linspace(off[e], off[e + 1] - 1, 16).astype(np.int64)
+        xd = M.mx_roundtrip(np32(p["x"][torch.as_tensor(r["token_of"][rows], device="cuda")]),
+                            axis=1)
+        u = np.zeros((len(rows), w.h))
+        for c0 in range(0, w.h, 2048):  # W1[e] in column slices (blocks run down columns)
+            sl = np32(p["w1"][e, :, c0:c0 + 2048])
+            u[:, c0:c0 + 2048] = xd @ M.mx_roundtrip(sl, axis=0)
+        hc, hs = M.mx_quantize(O.gelu_tanh(u), axis=1)
+        w2d = M.mx_roundtrip(np32(p["w2"][e][:, torch.as_tensor(ocols, device="cuda")]), axis=0)
+        o = M.mx_dequantize(hc, hs, axis=1) @ w2d
+        oc, osc = M.mx_quantize(o, axis=1)
+        check_mx_close(f"h rows of expert {e}", u8(buf.h_q[torch.as_tensor(rows, device="cuda")]),
+                       op_rows(buf.h_s, nmax, w.h)[rows], hc, hs)
+        gout = u8(buf.out_q[torch.as_tensor(rows, device="cuda")])[:, ocols]
+        gsc = u8(buf.out_s[torch.as_tensor(rows, device="cuda")])[:, blocks]
+        check_mx_close(f"out rows of expert {e}", gout, gsc, oc, osc, min_exact=0.9,
+                       units=16.0)
+    # y against combine's definition on the GPU's own FP8 outputs
+    y = buf.y.cpu().to(torch.float64).numpy()
+    for t in toks[:64]:
+        acc = np.zeros(w.H)
+        for k in range(w.K):
+            rr = int(ro[t, k])
+            if rr >= 0:
+                d = M.mx_dequantize(u8(buf.out_q[rr])[None], u8(buf.out_s[rr])[None], axis=1)[0]
+                acc += float(buf.topk_w[t, k].item()) * d
+        mag = np.zeros(w.H)
+        for k in range(w.K):
+            rr = int(ro[t, k])
+            if rr >= 0:
+                d = M.mx_dequantize(u8(buf.out_q[rr])[None], u8(buf.out_s[rr])[None], axis=1)[0]
+                mag += abs(float(buf.topk_w[t, k].item())) * np.abs(d)
+        # bf16 rounding of the sum, plus fp32 rounding of the terms
+        err = np.abs(y[t] - acc) / (2.0 ** -8 * np.abs(acc) + 2.0 ** -20 * mag + 1e-30)
+        assert err.max() <= 1.0, (t, err.max())
+    say(f"  y of 64 tokens = bf16(sum_k w deq(out)); N = {N}")
