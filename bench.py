@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer fwd tokens/s on 1 GPU + grouped-GEMM MFMA% and permute HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector / MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -47,21 +48,25 @@ def parse():
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--alpha", type=float, default=0.01,
                     help="aux-loss coefficient of the backward leg")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the MXFP8-forward leg")
+    ap.add_argument("--fp8-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run one device copy of BYTES bytes "
                          "(the known-size kernel that calibrates HBM counters)")
     return ap.parse_args()
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kernel: str = "bf16"):
     """HBM bytes per grouped-GEMM launch from the committed rocprofv3 --pmc
     summary, if it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.json")
+    stem = "grouped_gemm" if kernel == "bf16" else f"grouped_gemm_{kernel}"
+    p = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     from mixture_experts_layer_08_amd.profiling import gemm_source_hash
-    if d.get("gemm_source_sha256_16") != gemm_source_hash():
+    if d.get("gemm_source_sha256_16") != gemm_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -90,6 +95,77 @@ def cpu_baseline(w, p, n_tokens: int):
                    f"numpy oracle forward (router, routing with capacity on the sub-batch, "
                    f"expert FFN, combine) in {dt:.1f} s; BLAS threads {threads}, "
                    f"host cpu_count {os.cpu_count()}"),
+    }
+
+
+def mxfp8_leg(w, p, dev, steps: int, warmup: int) -> dict:
+    """The MXFP8 forward (FP8 dispatch, expert GEMMs and combine; routing
+    unchanged), each call bracketed by HIP events on the launch stream.  The
+    expert weights are quantised once before the timed region, as a model
+    would store them."""
+    import torch
+
+    from mixture_experts_layer_08_amd import counters, layer
+
+    stream = torch.cuda.current_stream()
+    mw = layer.MxWeights.quantize(w, p, stream)
+    buf = layer.MxBuffers.allocate(w, device=dev)
+    for _ in range(warmup):
+        layer.forward_mxfp8(buf, p, mw, stream)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(6)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        m = marks[s]
+        m[0].record(stream)
+        layer.route(buf, p, stream)
+        m[1].record(stream)
+        layer.aux_loss(buf, stream)
+        m[2].record(stream)
+        layer.permute_mxfp8(buf, p, stream)
+        m[3].record(stream)
+        layer.expert_ffn_mxfp8(buf, mw, stream)
+        m[4].record(stream)
+        layer.combine_mxfp8(buf, stream)
+        m[5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def stage_ms(i):
+        return sum(marks[s][i].elapsed_time(marks[s][i + 1]) for s in range(steps)) / steps
+
+    route_ms, aux_ms, perm_ms, ffn_ms, comb_ms = (stage_ms(i) for i in range(5))
+    N = int(buf.offsets[-1].item())
+    launches = 2 + (2 if w.hs else 0)
+    flop = 2 * counters.grouped_gemm_flop_per_launch(N, w.H, w.h)
+    if w.hs:
+        flop += 2 * counters.grouped_gemm_flop_per_launch(w.T, w.H, w.hs)
+    tflops = flop / (ffn_ms * 1e-3) / 1e12
+    perm_bytes = counters.permute_mx8_bytes(w.T, N, w.H, w.K, bool(w.hs))
+    comb_bytes = counters.combine_mx8_bytes(w.T, N, w.H, w.K, bool(w.hs))
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    step_ms = wall * 1e3 / steps
+    return {
+        "tokens_per_s": w.T / (step_ms * 1e-3),
+        "ms_per_step": step_ms,
+        "steps": steps,
+        "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute_mxfp8": perm_ms,
+                      "expert_ffn_mxfp8": ffn_ms, "combine_mxfp8": comb_ms},
+        "grouped_gemm": {"kernel": "k_grouped_gemm_mx8", "bound": "mfma", "achieved": tflops,
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / PEAK_FP8_TFLOPS, "flop_per_launch": flop / launches,
+                         "traffic": traffic_from_profile(w.name, "mx8"),
+                         "avg_launch_ms": ffn_ms / launches},
+        "hbm": {
+            "permute_mxfp8": {"GB/s": gbs(perm_bytes, perm_ms),
+                              "frac": gbs(perm_bytes, perm_ms) / PEAK_HBM_GBS,
+                              "bytes": perm_bytes},
+            "combine_mxfp8": {"GB/s": gbs(comb_bytes, comb_ms),
+                              "frac": gbs(comb_bytes, comb_ms) / PEAK_HBM_GBS,
+                              "bytes": comb_bytes},
+        },
+        "format": "MXFP8: E4M3 codes, one E8M0 scale per 32 values along the contraction",
     }
 
 
@@ -265,6 +341,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not a.no_fp8 and w.dtype == "bf16":
+        res["mxfp8"] = mxfp8_leg(w, p, dev, a.fp8_steps, min(a.warmup, 3))
+        torch.cuda.empty_cache()
     if not a.no_backward:
         del buf
         torch.cuda.empty_cache()

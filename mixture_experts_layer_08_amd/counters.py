@@ -56,3 +56,27 @@ def router_bytes(T: int, H: int, E: int, K: int, b: int) -> int:
     """Router kernel: x read once, router weight read once, fp32 logits and
     the top-k ids/weights written."""
     return T * H * b + H * E * b + 4 * T * E + 8 * T * K
+
+
+# -- the MXFP8 forward (one E8M0 scale byte per 32 E4M3 code bytes) ----------
+
+def mx_bytes(values: int) -> int:
+    """Bytes of `values` MXFP8 values: one code byte each plus one scale byte
+    per block of 32."""
+    return values + values // 32
+
+
+def permute_mx8_bytes(T: int, n_kept: int, H: int, K: int, shared: bool) -> int:
+    """Quantising dispatch: each bf16 token row read once, each kept row
+    written once in MXFP8 (and every token's own row when a shared expert
+    reads it), plus the int32 routing traffic of the bf16 dispatch."""
+    rows_out = n_kept + (T if shared else 0)
+    return T * H * 2 + mx_bytes(rows_out * H) + 4 * (2 * T * K + n_kept)
+
+
+def combine_mx8_bytes(T: int, n_kept: int, H: int, K: int, shared: bool) -> int:
+    """FP8 combine: each kept output row read once in MXFP8 (and the shared
+    expert's row), each bf16 token row written once, plus row_of and the fp32
+    weights."""
+    rows_in = n_kept + (T if shared else 0)
+    return mx_bytes(rows_in * H) + T * H * 2 + 8 * T * K

@@ -10,6 +10,9 @@ a plain device copy of known size profiled in the same run: the factor
         --write <write run>/p_counter_collection.csv \
         --copy-bytes 1073741824 --workload mixtral_bf16 \
         --out profiles/grouped_gemm_mixtral_bf16_traffic.json
+
+``--kernel mx8`` summarises the MXFP8 grouped GEMM of the same run instead
+(profiles/grouped_gemm_mx8_<workload>_traffic.json).
 """
 
 from __future__ import annotations
@@ -23,14 +26,22 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# the forward's row-major (NN) instantiations: GEMM1 with GELU and GEMM2
-GEMM_KERNEL = re.compile(r"k_grouped_gemm_bf16<\s*0\s*,")
+# Kernel families: the dispatches summarised and the sources their hash covers.
+#   bf16: the forward's row-major (NN) instantiations, GEMM1 with GELU and GEMM2
+#   mx8:  the MXFP8 grouped GEMM (both epilogues)
+KERNELS = {
+    "bf16": (re.compile(r"k_grouped_gemm_bf16<\s*0\s*,"), ("gemm.hip", "gemm_common.h")),
+    "mx8": (re.compile(r"k_grouped_gemm_mx8<"), ("gemm_mx8.hip", "gemm_common.h", "mx.h")),
+}
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
 
-def gemm_source_hash() -> str:
-    p = os.path.join(PKG, "csrc", "gemm.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def gemm_source_hash(kernel: str = "bf16") -> str:
+    """Hash of a grouped GEMM's sources (the kernel and its shared helpers)."""
+    h = hashlib.sha256()
+    for name in KERNELS[kernel][1]:
+        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def per_dispatch(path: str, counter: str):
@@ -46,14 +57,15 @@ def per_dispatch(path: str, counter: str):
     return {d: (meta[d][0], meta[d][1], v) for d, v in vals.items()}
 
 
-def traffic(fetch_csv, write_csv, copy_bytes, workload, out):
-    res = {"workload": workload, "gemm_source_sha256_16": gemm_source_hash(),
-           "copy_bytes": copy_bytes}
+def traffic(fetch_csv, write_csv, copy_bytes, workload, out, kernel="bf16"):
+    pattern = KERNELS[kernel][0]
+    res = {"workload": workload, "kernel": pattern.pattern,
+           "gemm_source_sha256_16": gemm_source_hash(kernel), "copy_bytes": copy_bytes}
     totals = {}
     for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
                                 ("write", write_csv, "WRITE_SIZE")):
         d = per_dispatch(path, counter)
-        gemm_ids = [i for i, (k, g, v) in d.items() if GEMM_KERNEL.search(k)]
+        gemm_ids = [i for i, (k, g, v) in d.items() if pattern.search(k)]
         if not gemm_ids:
             raise SystemExit(f"{path}: no grouped-GEMM dispatch")
         gemms = [d[i][2] for i in gemm_ids]
@@ -84,8 +96,9 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--kernel", choices=sorted(KERNELS), default="bf16")
     a = ap.parse_args()
-    traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out)
+    traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out, a.kernel)
 
 
 if __name__ == "__main__":
