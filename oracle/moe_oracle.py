@@ -414,13 +414,19 @@ def route_backward(logits, ids, w, dw, E: int, K: int, alpha: float):
 
 
 def backward(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, dy, K: int, cf: float,
-             alpha: float = 0.0, logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+             alpha: float = 0.0, logits: Optional[np.ndarray] = None,
+             tau: float = 1.0) -> Dict[str, np.ndarray]:
     """Every gradient of L = <dy, y> + alpha * aux for one layer forward.
 
     Routing is that of :func:`forward` with the same arguments (from the given
     logits when passed).  Returns dx, dw_r, db_r, dw1, dw2, dws1, dws2 and the
     intermediates d_out (rows of the packed expert outputs), d_w (routing
     weights), d_xp (rows of the packed inputs) and d_logits.
+
+    With a temperature (or noise) the given ``logits`` are the selection
+    scores z = (x W_r + b + g) / tau the forward routed on: d_logits is dL/dz,
+    and the router's own gradients use dL/d(x W_r + b) = dL/dz / tau (the noise
+    g does not depend on any parameter; the noisy router of [infra] 3.1).
     """
     fw = forward(x, w_r, b_r, w1, w2, ws1, ws2, K=K, cf=cf, logits=logits)
     E = w1.shape[0]
@@ -444,9 +450,10 @@ def backward(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, dy, K: int, cf: float,
     l_sel = np.asarray(logits, dtype=np.float64) if logits is not None \
         else fw["logits_oracle"].astype(np.float32).astype(np.float64)
     dl = route_backward(l_sel, fw["ids"], fw["w"], dw, E, K, alpha)
-    dx += dl @ np.asarray(w_r, dtype=np.float64).T
-    dw_r = x64.T @ dl
-    db_r = dl.sum(axis=0)
+    dl_raw = dl / float(tau)
+    dx += dl_raw @ np.asarray(w_r, dtype=np.float64).T
+    dw_r = x64.T @ dl_raw
+    db_r = dl_raw.sum(axis=0)
     dws1 = dws2 = None
     if ws1 is not None:
         dxs, dws1, dws2 = ffn_backward(x64, ws1, ws2, dy)
