@@ -66,6 +66,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_FLAG_TRAIN 2u      /* moe_expert_ffn keeps the GELU pre-activations in the
                                   workspace for moe_expert_ffn_backward, and the
                                   workspace also holds the backward's scratch */
+#define MOE_FLAG_GUMBEL 4u     /* moe_route adds Gumbel noise drawn from
+                                  (noise_seed, noise_offset) to the logits */
 
 typedef struct {
   int32_t T;        /* tokens in the batch                                   */
@@ -77,6 +79,10 @@ typedef struct {
   float capacity_factor; /* > 0: C = ceil(cf*T*K/E); <= 0: no limit (C = T)  */
   int32_t dtype;    /* moe_dtype                                             */
   uint32_t flags;   /* MOE_FLAG_*                                            */
+  float router_tau; /* router softmax temperature tau > 0; 0 means 1          */
+  uint64_t noise_seed;   /* MOE_FLAG_GUMBEL: Philox key word 0               */
+  uint64_t noise_offset; /* MOE_FLAG_GUMBEL: Philox counter word 2 (advance it
+                            every step for fresh noise)                       */
 } moe_shape;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -104,16 +110,24 @@ size_t moe_workspace_size(const moe_shape* s);
  * ([infra] 3.1 and 4.2; [comm] 1.1 step 1; inference top-k on logits,
  * [infra] 5.2 tip 4).
  *
+ * Selection scores z = (l + g) / tau with l = x*W_r + b (fp32 accumulation),
+ * tau = router_tau, and g = 0 unless MOE_FLAG_GUMBEL, when g is the Gumbel
+ * noise of [infra] 3.1: g = -log(-log(U + 1e-9) + 1e-9), U[t, e] word e % 4
+ * of the Philox4x64-10 block with counter (t, e / 4, noise_offset, 0) and key
+ * (noise_seed, 0), as (word >> 40) * 2^-24.  Top-k, the softmax, the weights
+ * and the aux loss's probabilities all act on z.
+ *
  *   x        [T,H]   token rows (dtype)
  *   w_router [H,E]   router weight (dtype)
  *   b_router [E]     fp32 router bias, or NULL for none
- *   logits   [T,E]   fp32 out: x*W_r + b accumulated in fp32.  With
- *                    MOE_FLAG_LOGITS_IN it is an input and x / w_router /
- *                    b_router are ignored (may be NULL).
- *   topk_ids [T,K]   int32 out: the K experts with the largest logits, slot 0
- *                    the largest; equal logits go to the lower expert index.
+ *   logits   [T,E]   fp32 out: z (= x*W_r + b with no noise and tau 1).  With
+ *                    MOE_FLAG_LOGITS_IN it is an input, taken as z (no noise
+ *                    or temperature applied), and x / w_router / b_router are
+ *                    ignored (may be NULL).
+ *   topk_ids [T,K]   int32 out: the K experts with the largest z, slot 0 the
+ *                    largest; equal scores go to the lower expert index.
  *   topk_w   [T,K]   fp32 out: p[t,e]/sum_{chosen} p[t,e'] with p the softmax
- *                    of the logits row (no noise, temperature 1).
+ *                    of the z row.
  *   ws               workspace; receives per-block expert histograms, in-block
  *                    ranks and per-block softmax column sums.
  * Logits must be finite (not checked).
@@ -329,14 +343,18 @@ moe_status moe_combine_backward(const moe_shape* s, const void* dy, const void* 
                                 float* d_topk_w, void* stream);
 
 /*
- * moe_route_backward - gradient of the router.
- *   d_logits[t, e] = [e chosen as slot k] w_k (d_w_k - sum_j w_j d_w_j)
- *                    + alpha * (E/T) p[t,e] (f_e - sum_e' f_e' p[t,e'])
- * with w = topk_w, p the softmax of the logits row and f_e = counts[e]/(T*K);
+ * moe_route_backward - gradient of the router.  With z the selection scores
+ * moe_route stored in `logits` (p their softmax, w = topk_w, f_e =
+ * counts[e]/(T*K)):
+ *   d_z[t, e] = [e chosen as slot k] w_k (d_w_k - sum_j w_j d_w_j)
+ *               + alpha * (E/T) p[t,e] (f_e - sum_e' f_e' p[t,e'])
+ * and, since z = (l + g) / tau and the noise depends on no parameter,
+ *   d_logits = d_z / tau        (the gradient of l = x*W_r + b; tau = 1 with
+ *                                MOE_FLAG_LOGITS_IN)
  * then d_w_router = x^T d_logits and d_b_router = sum_t d_logits[t] (fp32,
  * fixed summation order).
  *
- *   x [T,H], w_router [H,E]      as given to moe_route (dtype)
+ *   x [T,H]                      as given to moe_route (dtype)
  *   logits, topk_ids, topk_w     from moe_route; counts from moe_permute
  *   d_topk_w  [T,K]              from moe_combine_backward
  *   alpha                        aux-loss coefficient (0: no aux term)

@@ -24,6 +24,7 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_LOGITS_IN = 1
 MOE_FLAG_TRAIN = 2
+MOE_FLAG_GUMBEL = 4
 
 # Every symbol include/moe.h declares.
 EXPORTS = (
@@ -47,12 +48,15 @@ class moe_shape(ctypes.Structure):
         ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
         ("K", ctypes.c_int32), ("h_exp", ctypes.c_int32), ("h_shared", ctypes.c_int32),
         ("capacity_factor", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("flags", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32), ("router_tau", ctypes.c_float),
+        ("noise_seed", ctypes.c_uint64), ("noise_offset", ctypes.c_uint64),
     ]
 
 
-def make_shape(T, H, E, K, h_exp, h_shared=0, capacity_factor=0.0, dtype=MOE_BF16, flags=0):
-    return moe_shape(T, H, E, K, h_exp, h_shared, capacity_factor, dtype, flags)
+def make_shape(T, H, E, K, h_exp, h_shared=0, capacity_factor=0.0, dtype=MOE_BF16, flags=0,
+               router_tau=0.0, noise_seed=0, noise_offset=0):
+    return moe_shape(T, H, E, K, h_exp, h_shared, capacity_factor, dtype, flags, router_tau,
+                     noise_seed, noise_offset)
 
 
 _lib = None

@@ -81,6 +81,9 @@ T* at(void* ws, size_t off) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The router temperature (0 in the shape means 1).
+float router_tau_of(const moe_shape* s) { return s->router_tau > 0.0f ? s->router_tau : 1.0f; }
+
 // GEMM over rows (NN / NT): C [rows][N] = A [rows][Kd] * B_g (or B_g^T).
 GemmArgs rows_gemm(int layout, int epi, const void* A, const void* B, void* C, void* E,
                    const int32_t* offsets, int G, int fixed_rows, int max_rows, int Kd, int N) {
@@ -179,8 +182,10 @@ moe_status moe_check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->K > s->E) return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (s->flags & ~(MOE_FLAG_LOGITS_IN | MOE_FLAG_TRAIN)) return MOE_ERR_INVALID_ARG;
+  if (s->flags & ~(MOE_FLAG_LOGITS_IN | MOE_FLAG_TRAIN | MOE_FLAG_GUMBEL))
+    return MOE_ERR_INVALID_ARG;
   if (!isfinite(s->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(s->router_tau) || s->router_tau < 0.0f) return MOE_ERR_INVALID_ARG;
   if (s->K > 8 || s->E > 256) return MOE_ERR_UNSUPPORTED;
   if (s->H % 8 || s->h_exp % 8 || s->h_shared % 8) return MOE_ERR_UNSUPPORTED;
   // int32 row indices and element offsets inside one row-block stay in range
@@ -235,6 +240,11 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_router,
   a.H = s->H;
   a.E = s->E;
   a.K = s->K;
+  a.noise.gumbel = (s->flags & MOE_FLAG_GUMBEL) != 0;
+  a.noise.tau = router_tau_of(s);
+  a.noise.active = a.noise.gumbel || a.noise.tau != 1.0f;
+  a.noise.seed = s->noise_seed;
+  a.noise.offset = s->noise_offset;
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -389,6 +399,7 @@ moe_status moe_route_backward(const moe_shape* s, const void* x, const float* lo
   const WsLayout L = ws_layout(s);
   RouteBwdArgs a{};
   a.bf16 = s->dtype == MOE_BF16;
+  a.inv_tau = (s->flags & MOE_FLAG_LOGITS_IN) ? 1.0f : 1.0f / router_tau_of(s);
   a.x = x;
   a.logits = logits;
   a.topk_ids = topk_ids;

@@ -124,14 +124,17 @@ __global__ __launch_bounds__(256) void k_combine_bwd(
 }
 
 // Gate gradient, one wave per token; lane l holds experts l, l+64, l+128,
-// l+192 (E <= 256).
-//   d_l[e] = alpha (E/T) p_e (f_e - sum_e' f_e' p_e')       (aux term)
+// l+192 (E <= 256).  With p the softmax of the selection scores z that the
+// forward stored in `logits`:
+//   d_z[e] = alpha (E/T) p_e (f_e - sum_e' f_e' p_e')       (aux term)
 //          + [e = ids[k]] w_k (d_w_k - sum_j w_j d_w_j)    (weights term)
+// and the output is d_l = d_z / tau, the gradient of the router GEMM output
+// (z = (l + g) / tau; the noise g does not depend on any parameter).
 __global__ __launch_bounds__(256) void k_route_bwd_dl(
     const float* __restrict__ logits, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, const float* __restrict__ d_topk_w,
-    const int32_t* __restrict__ counts, float alpha, float* __restrict__ d_logits, int T, int E,
-    int K) {
+    const int32_t* __restrict__ counts, float alpha, float inv_tau, float* __restrict__ d_logits,
+    int T, int E, int K) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform; no barrier in this kernel
   const int lane = threadIdx.x & 63;
@@ -185,10 +188,11 @@ __global__ __launch_bounds__(256) void k_route_bwd_dl(
         if (lane + 64 * i == e) dl[i] += g;
     }
   }
+  // dL/dz -> dL/dl for z = (l + g) / tau (inv_tau = 1 for the plain router)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) d_logits[(size_t)t * E + e] = dl[i];
+    if (e < E) d_logits[(size_t)t * E + e] = dl[i] * inv_tau;
   }
 }
 
@@ -457,7 +461,8 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t st) {
 
 hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st) {
   k_route_bwd_dl<<<(a.T + 3) / 4, 256, 0, st>>>(a.logits, a.topk_ids, a.topk_w, a.d_topk_w,
-                                                  a.counts, a.alpha, a.d_logits, a.T, a.E, a.K);
+                                                  a.counts, a.alpha, a.inv_tau, a.d_logits, a.T,
+                                                  a.E, a.K);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int chunk = route_bwd_chunk(a.E);

@@ -16,6 +16,16 @@ namespace moe {
 // per-block histograms / in-block ranks the permutation builds on.
 constexpr int kRouteBlock = 64;
 
+// Router variant of section 3.1 of the dpshk.com "MoE module infra notes":
+// selection scores (logits + Gumbel noise) / tau.  active = gumbel || tau != 1.
+struct RouterNoise {
+  int active;
+  int gumbel;
+  float tau;
+  unsigned long long seed;
+  unsigned long long offset;
+};
+
 struct RouteArgs {
   bool bf16;
   bool logits_in;
@@ -30,6 +40,7 @@ struct RouteArgs {
   float* psum;         // [E][nblk]
   int32_t* lrank;      // [T][K]
   int T, H, E, K;
+  RouterNoise noise;
 };
 
 size_t route_lds_bytes(int E);
@@ -192,6 +203,7 @@ inline bool route_bwd_uses_mfma(bool bf16, int E) { return bf16 && E > 32; }
 
 struct RouteBwdArgs {
   bool bf16;
+  float inv_tau;       // d_logits = (dL/dz) / tau: the gradient of the router GEMM output
   const void* x;
   const float* logits;
   const int32_t* topk_ids;

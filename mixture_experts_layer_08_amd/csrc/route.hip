@@ -44,6 +44,62 @@ __global__ __launch_bounds__(256) void k_transpose_router(const bf16* __restrict
 // Shared epilogue.  s_logit holds the block's fp32 logits, row stride ES.
 // Called by all 256 threads after a barrier that published s_logit.  s_ids
 // is [kRouteBlock][8], s_mask [E] (scratch).
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): each round multiplies words 0 and 2
+// by the Philox multipliers, mixes the halves with words 1, 3 and the key,
+// then bumps the key by the two Weyl constants.
+__device__ __forceinline__ void philox4x64_10(unsigned long long (&c)[4], unsigned long long k0,
+                                              unsigned long long k1) {
+  const unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const unsigned long long hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const unsigned long long n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// The noisy router of section 3.1 of the dpshk.com "MoE module infra notes":
+// selection scores z = (l + g) / tau with Gumbel noise g = -log(-log(U + 1e-9)
+// + 1e-9).  U[t, e] is word e % 4 of the Philox block with counter
+// (t, e / 4, offset, 0) and key (seed, 0), as (word >> 40) * 2^-24 (24 bits,
+// on [0, 1)).  Applied in place to a block's logits tile in LDS (ES floats
+// per token row), before selection.
+__device__ void route_noise(float* s_logit, int ES, int t0, int nt, int E,
+                            const RouterNoise& nz) {
+  const int nq = (E + 3) >> 2;
+  for (int i = threadIdx.x; i < nt * nq; i += blockDim.x) {
+    const int t = i / nq, q = i - t * nq;
+    float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (nz.gumbel) {
+      unsigned long long c[4] = {(unsigned long long)(t0 + t), (unsigned long long)q, nz.offset,
+                                 0ull};
+      philox4x64_10(c, nz.seed, 0ull);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float u = (float)(uint32_t)(c[j] >> 40) * 0x1p-24f;
+        g[j] = -logf(-logf(u + 1e-9f) + 1e-9f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * q + j;
+      if (e < E) {
+        float* v = s_logit + t * ES + e;
+        *v = (*v + g[j]) / nz.tau;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 __device__ void route_epilogue(float* s_logit, int ES, int32_t* s_ids,
                                unsigned long long* s_mask, int t0, int nt, int E, int K,
                                int nblk, float* __restrict__ logits_out,
@@ -161,7 +217,7 @@ __global__ __launch_bounds__(256) void k_route_bf16(
     const bf16* __restrict__ x, const bf16* __restrict__ wT, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, float* __restrict__ psum, int32_t* __restrict__ lrank, int T,
-    int H, int E, int K, int nblk) {
+    int H, int E, int K, int nblk, RouterNoise nz) {
   extern __shared__ __attribute__((aligned(16))) float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
   __shared__ unsigned long long s_mask[256];
@@ -275,6 +331,7 @@ __global__ __launch_bounds__(256) void k_route_bf16(
     }
   }
   __syncthreads();
+  if (nz.active) route_noise(s_logit, ES, t0, nt, E, nz);
   route_epilogue(s_logit, ES, s_ids, s_mask, t0, nt, E, K, nblk, logits, topk_ids, topk_w,
                  hist, psum, lrank);
 }
@@ -283,7 +340,7 @@ __global__ __launch_bounds__(256) void k_route_f32(
     const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, float* __restrict__ psum, int32_t* __restrict__ lrank, int T,
-    int H, int E, int K, int nblk) {
+    int H, int E, int K, int nblk, RouterNoise nz) {
   extern __shared__ float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
   __shared__ unsigned long long s_mask[256];
@@ -298,6 +355,7 @@ __global__ __launch_bounds__(256) void k_route_f32(
     s_logit[t * ES + e] = acc + (bias ? bias[e] : 0.0f);
   }
   __syncthreads();
+  if (nz.active) route_noise(s_logit, ES, t0, nt, E, nz);
   route_epilogue(s_logit, ES, s_ids, s_mask, t0, nt, E, K, nblk, logits, topk_ids, topk_w,
                  hist, psum, lrank);
 }
@@ -355,7 +413,7 @@ static hipError_t launch_route_bf16(const RouteArgs& a, int nblk, hipStream_t st
   if (err != hipSuccess) return err;
   k_route_bf16<CT><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.wT, a.bias, a.logits,
                                            a.topk_ids, a.topk_w, a.hist, a.psum, a.lrank, a.T,
-                                           a.H, a.E, a.K, nblk);
+                                           a.H, a.E, a.K, nblk, a.noise);
   return hipGetLastError();
 }
 
@@ -373,7 +431,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     if ((err = allow_lds(k_route_f32, lds)) != hipSuccess) return err;
     k_route_f32<<<nblk, 256, lds, st>>>((const float*)a.x, (const float*)a.w_r, a.bias,
                                         a.logits, a.topk_ids, a.topk_w, a.hist, a.psum,
-                                        a.lrank, a.T, a.H, a.E, a.K, nblk);
+                                        a.lrank, a.T, a.H, a.E, a.K, nblk, a.noise);
     return hipGetLastError();
   }
   const int CTp = route_col_tiles(a.E);

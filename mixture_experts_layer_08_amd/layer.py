@@ -18,10 +18,18 @@ from . import binding as B
 from .inputs import Workload
 
 
-def shape_of(w: Workload, logits_in: bool = False, train: bool = False) -> B.moe_shape:
+def shape_of(w: Workload, logits_in: bool = False, train: bool = False,
+             router_tau: float = 0.0, noise: Optional[tuple] = None) -> B.moe_shape:
+    """The C shape of workload w.  router_tau: softmax temperature (0 = 1);
+    noise: (seed, offset) turns on the router's Gumbel noise."""
     flags = (B.MOE_FLAG_LOGITS_IN if logits_in else 0) | (B.MOE_FLAG_TRAIN if train else 0)
+    seed = offset = 0
+    if noise is not None:
+        flags |= B.MOE_FLAG_GUMBEL
+        seed, offset = noise
     return B.make_shape(w.T, w.H, w.E, w.K, w.h, w.hs, w.cf,
-                        B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32, flags)
+                        B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32, flags, router_tau,
+                        seed, offset)
 
 
 @dataclasses.dataclass
@@ -47,8 +55,9 @@ class MoeBuffers:
 
     @staticmethod
     def allocate(w: Workload, device="cuda", logits_in: bool = False,
-                 train: bool = False) -> "MoeBuffers":
-        s = shape_of(w, logits_in, train)
+                 train: bool = False, router_tau: float = 0.0,
+                 noise: Optional[tuple] = None) -> "MoeBuffers":
+        s = shape_of(w, logits_in, train, router_tau, noise)
         st = B.moe_check_shape(s)
         if st != B.MOE_OK:
             raise B.MoeError("moe_check_shape", st, B.moe_status_string(st))

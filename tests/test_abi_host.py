@@ -64,7 +64,11 @@ def shape(**kw):
     ({"h_shared": 12}, B.MOE_ERR_UNSUPPORTED),
     ({"h_shared": -8}, B.MOE_ERR_INVALID_ARG),
     ({"dtype": 7}, B.MOE_ERR_INVALID_ARG),
-    ({"flags": 4}, B.MOE_ERR_INVALID_ARG),
+    ({"flags": 8}, B.MOE_ERR_INVALID_ARG),
+    ({"flags": B.MOE_FLAG_GUMBEL, "noise_seed": 2 ** 64 - 1, "noise_offset": 5}, B.MOE_OK),
+    ({"router_tau": 0.8}, B.MOE_OK),
+    ({"router_tau": -1.0}, B.MOE_ERR_INVALID_ARG),
+    ({"router_tau": float("inf")}, B.MOE_ERR_INVALID_ARG),
     ({"flags": B.MOE_FLAG_TRAIN}, B.MOE_OK),
     ({"flags": B.MOE_FLAG_TRAIN | B.MOE_FLAG_LOGITS_IN}, B.MOE_OK),
     ({"capacity_factor": float("nan")}, B.MOE_ERR_INVALID_ARG),
@@ -73,6 +77,29 @@ def shape(**kw):
 ])
 def test_check_shape(lib, kw, expect):
     assert B.moe_check_shape(shape(**kw)) == expect
+
+
+def test_shape_struct_layout_matches_header(tmp_path):
+    """The ctypes moe_shape has the C struct's size and field offsets (a small
+    C program built from include/moe.h with the host compiler prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in B.moe_shape._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"moe.h\"\nint main(void){\n"
+        + f'printf("%zu\\n", sizeof(moe_shape));\n'
+        + "".join(f'printf("%zu\\n", offsetof(moe_shape, {f}));\n' for f in fields)
+        + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, str(src), "-I", os.path.join(ROOT, "include"), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(B.moe_shape)
+    assert out[1:] == [getattr(B.moe_shape, f).offset for f in fields]
 
 
 @pytest.mark.parametrize("T,K,E,cf", [
