@@ -169,6 +169,38 @@ def mxfp8_leg(w, p, dev, steps: int, warmup: int) -> dict:
     }
 
 
+def router_noise_leg(w, p, dev, steps: int) -> dict:
+    """The router stage with the noisy-router variant (Gumbel noise from the
+    on-device Philox stream, temperature 1.2) against the plain router, on
+    the same inputs; HIP events on the launch stream, the noise offset
+    advancing every step as in training."""
+    import torch
+
+    from mixture_experts_layer_08_amd import layer
+
+    stream = torch.cuda.current_stream()
+    plain = layer.MoeBuffers.allocate(w, device=dev)
+    noisy = layer.MoeBuffers.allocate(w, device=dev, router_tau=1.2, noise=(2024, 0))
+
+    def time_route(buf, advance):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for i in range(3):
+            layer.route(buf, p, stream)
+        ev[0].record(stream)
+        for i in range(steps):
+            if advance:
+                buf.shape.noise_offset = i
+            layer.route(buf, p, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    ms_plain = time_route(plain, False)
+    ms_noisy = time_route(noisy, True)
+    return {"route_ms_plain": ms_plain, "route_ms_gumbel_tau1.2": ms_noisy,
+            "note": "moe_route (router GEMM, noise, softmax, top-k, block histograms)"}
+
+
 def backward_leg(w, p, dev, steps: int, warmup: int, alpha: float) -> dict:
     """Training step: forward with MOE_FLAG_TRAIN, then combine -> route ->
     expert FFN -> permute backward, each call bracketed by HIP events on the
@@ -341,6 +373,7 @@ def main():
         },
         "cpu_baseline": None,
     }
+    res["router_noise"] = router_noise_leg(w, p, dev, 20)
     if not a.no_fp8 and w.dtype == "bf16":
         res["mxfp8"] = mxfp8_leg(w, p, dev, a.fp8_steps, min(a.warmup, 3))
         torch.cuda.empty_cache()
