@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--alpha", type=float, default=0.01,
                     help="aux-loss coefficient of the backward leg")
+    ap.add_argument("--no-side-legs", action="store_true",
+                    help="skip the noisy-router and dense-FFN comparisons (counter runs)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the MXFP8-forward leg")
     ap.add_argument("--fp8-steps", type=int, default=20)
@@ -199,6 +201,41 @@ def router_noise_leg(w, p, dev, steps: int) -> dict:
     ms_noisy = time_route(noisy, True)
     return {"route_ms_plain": ms_plain, "route_ms_gumbel_tau1.2": ms_noisy,
             "note": "moe_route (router GEMM, noise, softmax, top-k, block histograms)"}
+
+
+def dense_ffn_ratio(w, p, dev, fwd_ms: float, steps: int) -> dict:
+    """The pages' single-GPU sanity check: the MoE forward's time over that of
+    one dense FFN of the same T, H, h (expert 0's weights) run through the
+    same grouped-GEMM kernel as a single segment of all T tokens (E = K = 1,
+    no capacity limit).  Top-2 does twice the dense FLOPs, so the ideal
+    ratio is about 2."""
+    import torch
+
+    from mixture_experts_layer_08_amd import binding as B
+    from mixture_experts_layer_08_amd.inputs import Workload
+
+    d = Workload("dense", T=w.T, H=w.H, E=1, K=1, h=w.h, cf=0.0, dtype=w.dtype)
+    s = B.make_shape(d.T, d.H, 1, 1, d.h, 0, 0.0, B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32)
+    dt = w.torch_dtype()
+    offsets = torch.tensor([0, w.T], dtype=torch.int32, device=dev)
+    hbuf = torch.empty((w.T, w.h), dtype=dt, device=dev)
+    out = torch.empty((w.T, w.H), dtype=dt, device=dev)
+    ws = torch.empty((B.moe_workspace_size(s),), dtype=torch.uint8, device=dev)
+    w1, w2 = p["w1"][:1], p["w2"][:1]
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        B.moe_expert_ffn(s, p["x"], offsets, w1, w2, hbuf, out, None, None, None, None, None, ws,
+                         stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        B.moe_expert_ffn(s, p["x"], offsets, w1, w2, hbuf, out, None, None, None, None, None, ws,
+                         stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    dense_ms = ev[0].elapsed_time(ev[1]) / steps
+    return {"dense_ffn_ms": dense_ms, "moe_forward_ms": fwd_ms, "ratio": fwd_ms / dense_ms,
+            "top_k": w.K, "note": "MoE forward / dense FFN of the same T, H, h (one segment)"}
 
 
 def backward_leg(w, p, dev, steps: int, warmup: int, alpha: float) -> dict:
@@ -373,7 +410,9 @@ def main():
         },
         "cpu_baseline": None,
     }
-    res["router_noise"] = router_noise_leg(w, p, dev, 20)
+    if not a.no_side_legs:
+        res["router_noise"] = router_noise_leg(w, p, dev, 20)
+        res["dense_ffn_sanity"] = dense_ffn_ratio(w, p, dev, ms_step, 10)
     if not a.no_fp8 and w.dtype == "bf16":
         res["mxfp8"] = mxfp8_leg(w, p, dev, a.fp8_steps, min(a.warmup, 3))
         torch.cuda.empty_cache()

@@ -87,6 +87,81 @@ def traffic(fetch_csv, write_csv, copy_bytes, workload, out, kernel="bf16"):
     print(json.dumps(res, indent=1))
 
 
+def per_kernel(path: str, counter: str, patterns: dict):
+    """{name: [values per dispatch]} for each kernel-name regex in patterns."""
+    d = per_dispatch(path, counter)
+    out = {n: [] for n in patterns}
+    for i in sorted(d):
+        k, _, v = d[i]
+        for n, rx in patterns.items():
+            if re.search(rx, k):
+                out[n].append(v)
+                break
+    return out, d
+
+
+# the bandwidth-bound kernels of the forward (bf16 and MXFP8 forms)
+HBM_KERNELS = {
+    "k_route_bf16": r"k_route_bf16<", "k_transpose_router": r"k_transpose_router",
+    "k_scan_blocks": r"k_scan_blocks", "k_permute": r"k_permute<", "k_permute_mx8": r"k_permute_mx8<",
+    "k_combine": r"k_combine<", "k_combine_mx8": r"k_combine_mx8<",
+}
+
+
+def hbm(fetch_csv, write_csv, copy_bytes, title, cmd, out):
+    """Markdown table: calibrated HBM bytes read and written per dispatch of
+    each bandwidth-bound kernel (mean over its dispatches)."""
+    rows = {}
+    for name, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("written", write_csv, "WRITE_SIZE")):
+        vals, d = per_kernel(path, counter, HBM_KERNELS)
+        copies = [v for i, (k, g, v) in d.items() if COPY_KERNEL in k]
+        factor = copy_bytes / (max(copies) * 1024.0)
+        for n, vs in vals.items():
+            if vs:
+                rows.setdefault(n, {})[name] = sum(vs) / len(vs) * 1024.0 * factor
+                rows[n]["dispatches"] = len(vs)
+        rows.setdefault("_factor", {})[name] = factor
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
+             cmd, "```", "",
+             "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor that maps the "
+             f"same counter on a {copy_bytes} B device copy in the same run to its known bytes "
+             f"(read {rows['_factor']['read']:.4f}, write {rows['_factor']['written']:.4f}).", "",
+             "| kernel | dispatches | MB read | MB written | MB total |", "|---|---|---|---|---|"]
+    for n in HBM_KERNELS:
+        if n in rows:
+            r = rows[n]
+            lines.append(f"| `{n}` | {r['dispatches']} | {r.get('read', 0) / 1e6:.1f} | "
+                         f"{r.get('written', 0) / 1e6:.1f} | "
+                         f"{(r.get('read', 0) + r.get('written', 0)) / 1e6:.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def mfma(csv_path, title, cmd, out, simds: int = 1024):
+    """Markdown table: per grouped-GEMM dispatch, SQ_VALU_MFMA_BUSY_CYCLES over
+    all SIMDs divided by (SIMDs x GRBM_GUI_ACTIVE per XCD): the fraction of
+    the kernel's cycles the MFMA pipes were busy."""
+    pats = {"k_grouped_gemm_bf16 (GEMM1, GELU)": r"k_grouped_gemm_bf16<\s*0\s*,\s*1>",
+            "k_grouped_gemm_bf16 (GEMM2)": r"k_grouped_gemm_bf16<\s*0\s*,\s*0>",
+            "k_grouped_gemm_mx8 (GEMM1, GELU)": r"k_grouped_gemm_mx8<1>",
+            "k_grouped_gemm_mx8 (GEMM2)": r"k_grouped_gemm_mx8<0>"}
+    busy, _ = per_kernel(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", pats)
+    gui, _ = per_kernel(csv_path, "GRBM_GUI_ACTIVE", pats)
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
+             cmd, "```", "",
+             f"MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over the {simds} SIMDs) / "
+             f"({simds} x GRBM_GUI_ACTIVE / 8), GRBM_GUI_ACTIVE being summed over the 8 XCDs.", "",
+             "| kernel | dispatches | MFMA busy cycles | GUI active cycles (per XCD) | MFMA busy |",
+             "|---|---|---|---|---|"]
+    for n in pats:
+        if busy[n]:
+            b = sum(busy[n]) / len(busy[n])
+            g = sum(gui[n]) / len(gui[n]) / 8.0
+            lines.append(f"| `{n}` | {len(busy[n])} | {b:.4g} | {g:.4g} | {b / (simds * g):.1%} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -97,8 +172,25 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--kernel", choices=sorted(KERNELS), default="bf16")
+    h = sub.add_parser("hbm")
+    h.add_argument("--fetch", required=True)
+    h.add_argument("--write", required=True)
+    h.add_argument("--copy-bytes", type=int, required=True)
+    h.add_argument("--title", required=True)
+    h.add_argument("--command", required=True, help="the command that produced the runs")
+    h.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--csv", required=True)
+    m.add_argument("--title", required=True)
+    m.add_argument("--command", required=True, help="the command that produced the run")
+    m.add_argument("--out", required=True)
     a = ap.parse_args()
-    traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out, a.kernel)
+    if a.cmd == "traffic":
+        traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out, a.kernel)
+    elif a.cmd == "hbm":
+        hbm(a.fetch, a.write, a.copy_bytes, a.title, a.command, a.out)
+    else:
+        mfma(a.csv, a.title, a.command, a.out)
 
 
 if __name__ == "__main__":
