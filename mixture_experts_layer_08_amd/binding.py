@@ -72,6 +72,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_08_amd.build`")
+        # torch ships its own HIP runtime (soname libamdhip64.so.7, loaded by
+        # torch's libraries under the name libamdhip64.so).  Loaded first, it
+        # satisfies libmoe.so's dependency, so the library and torch share one
+        # runtime and torch's streams and allocations are valid in our calls.
+        # Loaded the other way round, the process would hold two runtimes and
+        # every call with a torch stream would fail.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]

@@ -102,6 +102,22 @@ def test_shape_struct_layout_matches_header(tmp_path):
     assert out[1:] == [getattr(B.moe_shape, f).offset for f in fields]
 
 
+def test_library_shares_torchs_hip_runtime(lib):
+    """Loading the library before anything imports torch still leaves one HIP
+    runtime in the process: torch's copy, which owns the streams and
+    allocations the callers pass in (a second runtime rejects them)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from mixture_experts_layer_08_amd import binding\n"
+            "binding.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert r.stdout.split()[-1] == "1", r.stdout
+
+
 @pytest.mark.parametrize("T,K,E,cf", [
     (4096, 2, 8, 1.25), (32768, 2, 8, 1.25), (16384, 4, 64, 1.25), (32768, 2, 128, 0.0),
     (5, 1, 2, 1.0), (3, 1, 4, 0.5), (10, 2, 8, -1.0), (7, 3, 5, 0.3), (4, 1, 1, 1.25),
