@@ -88,7 +88,16 @@ typedef struct {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(int status);
 
-/* Validates `s` alone (sizes, dtype, flags); MOE_OK when the shape is usable. */
+/* Validates `s` alone (sizes, dtype, flags); MOE_OK when the shape is usable.
+ * MOE_ERR_INVALID_ARG for values outside the field ranges above, T < 1,
+ * K > E, unknown flags, a non-finite capacity factor or a negative or
+ * non-finite router_tau.  MOE_ERR_UNSUPPORTED for shapes the kernels do not
+ * cover: E > 256, K > 8, H / h_exp / h_shared not multiples of 8 or above
+ * 2^20, T*K >= 2^31, and in bf16 mode (whose GEMM reads each operand through
+ * a buffer range below 2 GiB) H*h_exp or H*h_shared above 2^30 - 8 elements,
+ * and with MOE_FLAG_TRAIN min(C, T)*max(H, h_exp) or T*max(H, h_shared, E)
+ * above that same count (the weight-gradient GEMMs read one segment's rows
+ * through one range). */
 moe_status moe_check_shape(const moe_shape* s);
 
 /* Expert capacity C: ceil(cf*T*K/E) computed in double for cf > 0, else T

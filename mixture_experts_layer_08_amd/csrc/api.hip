@@ -18,6 +18,19 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Largest byte range the kernels address through one buffer descriptor
+// (offsets are unsigned 32-bit and must stay below 2^31).
+constexpr long long kBufferBytes = 0x7ffffff0LL;
+
+// Expert capacity C of a shape whose fields have been validated.
+int64_t capacity_of(const moe_shape* s) {
+  const double cf = (double)s->capacity_factor;
+  if (cf <= 0.0) return s->T;
+  const double c = ceil(cf * (double)((long long)s->T * s->K) / (double)s->E);
+  if (c >= (double)s->T) return s->T;  // no expert can receive more than T
+  return (int64_t)c;
+}
+
 struct WsLayout {
   size_t wT, hist, psum, base, lrank;
   // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
@@ -193,16 +206,29 @@ moe_status moe_check_shape(const moe_shape* s) {
   if (TK >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->H > (1 << 20) || s->h_exp > (1 << 20) || s->h_shared > (1 << 20))
     return MOE_ERR_UNSUPPORTED;
+  if (s->dtype == MOE_BF16) {
+    // The bf16 grouped GEMM reads a whole weight matrix (one expert's, or
+    // the shared expert's) through one buffer descriptor, whose range stays
+    // below 2 GiB; so do the weight-gradient GEMMs of training mode with one
+    // segment's rows (an expert's at most min(C, T), the shared expert's
+    // and the router's T) times an operand width.
+    const long long lim = kBufferBytes / 2;  // bf16 elements
+    const long long H = s->H, h = s->h_exp, hs = s->h_shared;
+    if (H * h > lim || H * hs > lim) return MOE_ERR_UNSUPPORTED;
+    if (s->flags & MOE_FLAG_TRAIN) {
+      const long long seg = capacity_of(s);
+      const long long wide = H > h ? H : h;
+      long long wide_t = H > hs ? H : hs;
+      if (s->E > wide_t) wide_t = s->E;
+      if (seg * wide > lim || (long long)s->T * wide_t > lim) return MOE_ERR_UNSUPPORTED;
+    }
+  }
   return MOE_OK;
 }
 
 int64_t moe_capacity(const moe_shape* s) {
   if (moe_check_shape(s) != MOE_OK) return -1;
-  const double cf = (double)s->capacity_factor;
-  if (cf <= 0.0) return s->T;
-  const double c = ceil(cf * (double)((long long)s->T * s->K) / (double)s->E);
-  if (c >= (double)s->T) return s->T;  // no expert can receive more than T
-  return (int64_t)c;
+  return capacity_of(s);
 }
 
 int64_t moe_max_rows(const moe_shape* s) { return max_rows_of(s); }
@@ -675,8 +701,8 @@ moe_status check_mx_shape(const moe_shape* s) {
   const long long rows = moe_max_rows(s);
   const long long wide = s->H > s->h_exp ? s->H : s->h_exp;
   const long long wide_sh = s->H > s->h_shared ? s->H : s->h_shared;
-  if (rows * wide > 0x7ffffff0LL || (long long)s->T * wide_sh > 0x7ffffff0LL ||
-      (long long)s->H * s->h_exp > 0x7ffffff0LL || (long long)s->H * s->h_shared > 0x7ffffff0LL)
+  if (rows * wide > kBufferBytes || (long long)s->T * wide_sh > kBufferBytes ||
+      (long long)s->H * s->h_exp > kBufferBytes || (long long)s->H * s->h_shared > kBufferBytes)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

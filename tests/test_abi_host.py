@@ -74,6 +74,23 @@ def shape(**kw):
     ({"capacity_factor": float("nan")}, B.MOE_ERR_INVALID_ARG),
     ({"T": 1 << 28, "K": 8, "E": 8}, B.MOE_ERR_UNSUPPORTED),
     ({"K": 8, "E": 256, "T": 1}, B.MOE_OK),
+    # bf16: one weight matrix within 2^30 - 8 elements (a 2 GiB buffer range)
+    ({"H": 8192, "h_exp": 131064}, B.MOE_OK),
+    ({"H": 8192, "h_exp": 131080}, B.MOE_ERR_UNSUPPORTED),
+    ({"H": 8192, "h_exp": 131080, "dtype": B.MOE_F32}, B.MOE_OK),
+    ({"H": 8192, "h_shared": 131080}, B.MOE_ERR_UNSUPPORTED),
+    # training: one segment's rows times the wider operand, same limit
+    ({"T": 65528, "E": 1, "K": 1, "H": 64, "h_exp": 16384, "capacity_factor": 0.0,
+      "flags": B.MOE_FLAG_TRAIN}, B.MOE_OK),
+    ({"T": 65536, "E": 1, "K": 1, "H": 64, "h_exp": 16384, "capacity_factor": 0.0,
+      "flags": B.MOE_FLAG_TRAIN}, B.MOE_ERR_UNSUPPORTED),
+    ({"T": 65536, "E": 1, "K": 1, "H": 64, "h_exp": 16384, "capacity_factor": 0.0}, B.MOE_OK),
+    ({"T": 131072, "E": 2, "K": 1, "H": 64, "h_exp": 16384, "capacity_factor": 1.0,
+      "flags": B.MOE_FLAG_TRAIN}, B.MOE_ERR_UNSUPPORTED),
+    ({"T": 131072, "E": 2, "K": 1, "H": 64, "h_exp": 16376, "capacity_factor": 1.0,
+      "flags": B.MOE_FLAG_TRAIN}, B.MOE_OK),
+    ({"T": 1 << 24, "E": 256, "K": 1, "H": 64, "h_exp": 8, "capacity_factor": 1.0,
+      "flags": B.MOE_FLAG_TRAIN}, B.MOE_ERR_UNSUPPORTED),
 ])
 def test_check_shape(lib, kw, expect):
     assert B.moe_check_shape(shape(**kw)) == expect
