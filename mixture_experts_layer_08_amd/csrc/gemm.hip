@@ -107,7 +107,7 @@ template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv,
     bf16* Ep, const int32_t* __restrict__ offsets, int G, int fixed_rows,
-    int a_rows, int mt_bound, int M, int Kd, int N) {
+    int a_rows, int mt_bound, int M, int Kd, int N, int xcd_chunk) {
   constexpr bool kTN = LAYOUT == kGemmTN;
   constexpr bool kARows = !kTN;               // A in "rows" form
   constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
@@ -126,8 +126,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     row0 = mt * BM2;  // rows of C = columns of A
     rows = min(BM2, M - row0);
   } else {
-    if ((int)blockIdx.x >= mt_bound * nt_count) return;
-    decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
+    const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
+    if (tile >= mt_bound * nt_count) return;
+    decode_tile(tile, mt_bound, nt_count, mt, nt);
     if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
   }
   // The tile is wave-uniform; keep it in scalar registers so the buffer
@@ -490,7 +491,8 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k_grouped_gemm_bf16<LAYOUT, EPI><<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
       (const bf16*)a.A, (const bf16*)a.B, a.C, (bf16*)a.E, a.offsets, a.G, a.fixed_rows,
-      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N);
+      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N,
+      LAYOUT == kGemmTN ? 0 : xcd_chunk_for(ntc));
   return hipGetLastError();
 }
 

@@ -88,12 +88,13 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, uint8_t* __restrict__ C,
     uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int G, int fixed_rows,
-    int a_rows, int a_ld, int c_ld, int mt_bound, int Kd, int N) {
+    int a_rows, int a_ld, int c_ld, int mt_bound, int Kd, int N, int xcd_chunk) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx[];
   const int nt_count = (N + kMxBN - 1) / kMxBN;
-  if ((int)blockIdx.x >= mt_bound * nt_count) return;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
+  if (tile >= mt_bound * nt_count) return;
   int mt, nt, seg, row0, rows;
-  decode_tile(blockIdx.x, mt_bound, nt_count, mt, nt);
+  decode_tile(tile, mt_bound, nt_count, mt, nt);
   if (!find_segment<kMxBM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
   seg = __builtin_amdgcn_readfirstlane(seg);
   row0 = __builtin_amdgcn_readfirstlane(row0);
@@ -320,7 +321,7 @@ static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k_grouped_gemm_mx8<EPI><<<(unsigned)grid, kMxThreads, kMxSmem, st>>>(
       a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
-      a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N);
+      a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
   return hipGetLastError();
 }
 
