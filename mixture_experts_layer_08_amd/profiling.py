@@ -69,6 +69,9 @@ def traffic(fetch_csv, write_csv, copy_bytes, workload, out, kernel="bf16"):
         if not gemm_ids:
             raise SystemExit(f"{path}: no grouped-GEMM dispatch")
         gemms = [d[i][2] for i in gemm_ids]
+        by_name = collections.defaultdict(list)
+        for i in gemm_ids:
+            by_name[re.sub(r"\(.*", "", d[i][0]).replace("void ", "")].append(d[i][2])
         # the calibration copy is launched after the timed steps: the largest
         # copy dispatch after the last GEMM
         copies = [v for i, (k, g, v) in d.items() if COPY_KERNEL in k and i > max(gemm_ids)]
@@ -81,6 +84,8 @@ def traffic(fetch_csv, write_csv, copy_bytes, workload, out, kernel="bf16"):
         totals[name] = sum(gemms) / len(gemms) * 1024.0 * factor
         res[f"{name}_bytes_per_launch"] = totals[name]
         res[f"{name}_launches"] = len(gemms)
+        res[f"{name}_bytes_per_launch_by_kernel"] = {
+            k: sum(v) / len(v) * 1024.0 * factor for k, v in sorted(by_name.items())}
     res["hbm_bytes_per_launch"] = totals["fetch"] + totals["write"]
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
@@ -162,6 +167,43 @@ def mfma(csv_path, title, cmd, out, simds: int = 1024):
     print("\n".join(lines))
 
 
+def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16", top=14):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: the kernel
+    table, then the grouped GEMM's mean launch duration over every dispatch
+    of the run (from the trace) beside bench.py's event-timed mean launch of
+    the same run (from the JSON line it printed)."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    short = lambda n: re.sub(r"\(.*", "", n).replace("void ", "")[:70]
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
+             cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    pattern = KERNELS[kernel][0]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for r in csv.DictReader(open(trace_csv)) if pattern.search(r["Kernel_Name"])]
+    bench = None
+    for line in open(bench_log):
+        if line.startswith("{") and '"metric"' in line:
+            bench = json.loads(line)
+    lines.append("")
+    if durs:
+        lines.append(f"Grouped GEMM (`{pattern.pattern}`): {len(durs)} dispatches in the trace, "
+                     f"mean {sum(durs) / len(durs):.1f} us (warm-up included).")
+    if bench is not None:
+        g = bench["roofline"] if kernel == "bf16" else bench["mxfp8"]["grouped_gemm"]
+        lines.append(f"bench.py's event-timed mean launch over its timed steps in the same run: "
+                     f"{g['avg_launch_ms'] * 1e3:.1f} us ({g['achieved']:.1f} {g['unit']}, "
+                     f"{g['achieved'] / g['peak']:.1%} of {g['peak']:.0f}).")
+    if note:
+        lines += ["", note]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -184,11 +226,22 @@ def main():
     m.add_argument("--title", required=True)
     m.add_argument("--command", required=True, help="the command that produced the run")
     m.add_argument("--out", required=True)
+    st = sub.add_parser("stats")
+    st.add_argument("--stats", required=True, help="kernel_stats.csv of the run")
+    st.add_argument("--trace", required=True, help="kernel_trace.csv of the run")
+    st.add_argument("--bench-log", required=True, help="stdout of the profiled bench.py")
+    st.add_argument("--title", required=True)
+    st.add_argument("--command", required=True, help="the command that produced the run")
+    st.add_argument("--note", default="")
+    st.add_argument("--kernel", choices=sorted(KERNELS), default="bf16")
+    st.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "traffic":
         traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out, a.kernel)
     elif a.cmd == "hbm":
         hbm(a.fetch, a.write, a.copy_bytes, a.title, a.command, a.out)
+    elif a.cmd == "stats":
+        stats(a.stats, a.trace, a.bench_log, a.title, a.command, a.note, a.out, a.kernel)
     else:
         mfma(a.csv, a.title, a.command, a.out)
 
