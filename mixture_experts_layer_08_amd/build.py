@@ -66,7 +66,32 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_c_example(verbose)
     return LIB
+
+
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "forward.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "forward")
+
+
+def build_c_example(verbose: bool = True) -> str:
+    """The plain-C forward of tests/c_abi (host code only: gcc, the HIP
+    runtime API and libmoe.so, found next to it through an $ORIGIN rpath)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler for the C example")
+    rel = os.path.relpath(PKG, os.path.dirname(C_EXAMPLE))
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_EXAMPLE_SRC, "-o", C_EXAMPLE, "-L", PKG, "-lmoe", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C example build failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_EXAMPLE}")
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":
