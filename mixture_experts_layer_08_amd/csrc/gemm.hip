@@ -118,9 +118,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   if (kTN) {
     const int mt_count = (M + BM2 - 1) / BM2;
     const int per_seg = mt_count * nt_count;
-    if ((int)blockIdx.x >= G * per_seg) return;
-    seg = blockIdx.x / per_seg;
-    decode_tile(blockIdx.x - seg * per_seg, mt_count, nt_count, mt, nt);
+    const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
+    if (tile >= G * per_seg) return;
+    seg = tile / per_seg;
+    decode_tile(tile - seg * per_seg, mt_count, nt_count, mt, nt);
     k_begin = offsets ? offsets[seg] : 0;
     k_end = offsets ? offsets[seg + 1] : fixed_rows;
     row0 = mt * BM2;  // rows of C = columns of A
@@ -491,8 +492,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k_grouped_gemm_bf16<LAYOUT, EPI><<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
       (const bf16*)a.A, (const bf16*)a.B, a.C, (bf16*)a.E, a.offsets, a.G, a.fixed_rows,
-      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N,
-      LAYOUT == kGemmTN ? 0 : xcd_chunk_for(ntc));
+      a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N, xcd_chunk_for(ntc));
   return hipGetLastError();
 }
 

@@ -84,9 +84,10 @@ __device__ __forceinline__ int xcd_tile(int b, int grid, int chunk) {
   return b / span * span + (b % kXcds) * chunk + (b / kXcds) % chunk;
 }
 // The chunk a launch uses: 16 tiles for outputs at least 32 tiles wide.
-// Measured on the expert GEMMs (equal 8192-row segments): +4% for 14336
-// output columns, within -1.5..+0.4% for 4096, so narrower outputs keep the
-// plain order.
+// Measured on the expert GEMMs (equal 8192-row segments): +4% (row-major and
+// transposed-weight forms) and +5% (weight gradients) for 14336 output
+// columns, within -1.5..+0.4% for 4096, so narrower outputs keep the plain
+// order.
 inline int xcd_chunk_for(int nt_count) { return nt_count >= 32 ? 16 : 0; }
 
 constexpr uint32_t kOob = 0x80000000u;  // an offset past any num_records
