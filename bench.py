@@ -372,6 +372,17 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = traffic_from_profile(w.name)
 
+    # the expert FFN against its roofline, segment by segment: a segment of a
+    # few hundred rows is bound by reading its weights, not by MFMA
+    kept = buf.kept.cpu().tolist()
+    t_f, t_b, t_seg = counters.segment_roofline_s(kept, w.H, w.h, b, peak * 1e12,
+                                                  PEAK_HBM_GBS * 1e9, w.T if w.hs else 0, w.hs)
+    ffn_roofline = {"flop_bound_ms": t_f * 1e3, "byte_bound_ms": t_b * 1e3,
+                    "segment_bound_ms": t_seg * 1e3, "measured_ms": ffn_ms,
+                    "frac_of_segment_bound": t_seg * 1e3 / ffn_ms,
+                    "note": "segment bound: sum over expert segments of max(FLOP / MFMA peak, "
+                            "(weights + activations) bytes / HBM peak)"}
+
     perm_bytes = counters.permute_bytes(w.T, N, w.H, b, w.K)
     comb_bytes = counters.combine_kernel_bytes(w.T, N, w.H, b, w.K, bool(w.hs))
     route_bytes = counters.router_bytes(w.T, w.H, w.E, w.K, b)
@@ -398,6 +409,7 @@ def main():
                      "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "flop_per_launch": flop_per_launch, "avg_launch_ms": launch_s * 1e3},
+        "expert_ffn_roofline": ffn_roofline,
         "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute": perm_ms,
                       "expert_ffn": ffn_ms, "combine": comb_ms},
         "hbm": {

@@ -38,6 +38,33 @@ def grouped_gemm_flop_per_launch(n_rows: int, H: int, h: int) -> int:
     return 2 * n_rows * H * h
 
 
+def segment_roofline_s(rows, H: int, h: int, b: int, peak_flops: float, peak_bytes: float,
+                       shared_rows: int = 0, hs: int = 0):
+    """Roofline times of the expert FFN (GEMM1 + GEMM2) over segments of
+    `rows` kept rows (plus a shared expert over shared_rows tokens).
+
+    Per segment with n > 0 rows: 4*n*H*h FLOP and the bytes it must move at
+    least once, its two weight matrices (2*H*h*b) plus its activations (x
+    rows read, hidden rows written and read, output rows written:
+    2*n*(H + h)*b).  Returns (flop-bound s, byte-bound s, per-segment bound s)
+    where the first two total the whole launch pair and the last sums
+    max(flop time, byte time) over the segments, the bound of a segment that
+    is too small to reach the MFMA rate (a few hundred rows against its
+    weights) being its weight traffic.
+    """
+    segs = [(int(n), h) for n in rows if int(n) > 0]
+    if shared_rows > 0 and hs > 0:
+        segs.append((shared_rows, hs))
+    flop = byte = seg = 0.0
+    for n, width in segs:
+        f = 4.0 * n * H * width
+        m = (2.0 * H * width + 2.0 * n * (H + width)) * b
+        flop += f
+        byte += m
+        seg += max(f / peak_flops, m / peak_bytes)
+    return flop / peak_flops, byte / peak_bytes, seg
+
+
 def permute_bytes(T: int, n_kept: int, H: int, b: int, K: int) -> int:
     """Dispatch kernel: each token row read once, each kept row written once,
     plus the int32 routing ids read and row_of written (T*K each) and token_of
