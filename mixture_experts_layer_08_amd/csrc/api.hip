@@ -470,14 +470,8 @@ moe_status moe_expert_ffn_backward(const moe_shape* s, const void* xp, const int
         !aligned16(dy) || !aligned16(d_x_shared) || !aligned16(d_ws1) || !aligned16(d_ws2))
       return MOE_ERR_INVALID_ARG;
   }
-  // A weight-gradient GEMM addresses one expert's whole segment (or all T
-  // rows of the shared expert) through one 32-bit buffer range.
-  const long long elem = s->dtype == MOE_BF16 ? 2 : 4;
-  const long long seg_rows = moe_capacity(s);
-  const long long widest = s->H > s->h_exp ? s->H : s->h_exp;
-  if (seg_rows * widest * elem > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
-  if (shared && (long long)s->T * (s->H > s->h_shared ? s->H : s->h_shared) * elem > 0x7ffffff0LL)
-    return MOE_ERR_UNSUPPORTED;
+  // (moe_check_shape has already refused bf16 training shapes whose
+  // weight-gradient GEMMs would address more than one buffer range.)
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   const bool bf = s->dtype == MOE_BF16;
