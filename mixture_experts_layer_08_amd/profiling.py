@@ -167,11 +167,14 @@ def mfma(csv_path, title, cmd, out, simds: int = 1024):
     print("\n".join(lines))
 
 
-def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16", top=14):
+def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16", top=14,
+          window=None):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run: the kernel
-    table, then the grouped GEMM's mean launch duration over every dispatch
-    of the run (from the trace) beside bench.py's event-timed mean launch of
-    the same run (from the JSON line it printed)."""
+    table, then the grouped GEMM's mean launch duration from the trace beside
+    bench.py's event-timed mean launch of the same run (from the JSON line it
+    printed).  window = (start, count) restricts the trace mean to those
+    matching dispatches in dispatch order (e.g. the timed forward's launches
+    of a run that also has other legs); None takes every matching one."""
     rows = list(csv.DictReader(open(stats_csv)))
     short = lambda n: re.sub(r"\(.*", "", n).replace("void ", "")[:70]
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
@@ -183,16 +186,22 @@ def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16",
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.2f} |")
     pattern = KERNELS[kernel][0]
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            for r in csv.DictReader(open(trace_csv)) if pattern.search(r["Kernel_Name"])]
+    disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                  for r in csv.DictReader(open(trace_csv)) if pattern.search(r["Kernel_Name"]))
+    durs = [d / 1e3 for _, d in disp]
+    which = "every dispatch in the trace"
+    if window is not None:
+        start, count = window
+        durs = durs[start:start + count]
+        which = f"dispatches {start}..{start + len(durs) - 1} of the trace's {len(disp)} matching ones"
     bench = None
     for line in open(bench_log):
         if line.startswith("{") and '"metric"' in line:
             bench = json.loads(line)
     lines.append("")
     if durs:
-        lines.append(f"Grouped GEMM (`{pattern.pattern}`): {len(durs)} dispatches in the trace, "
-                     f"mean {sum(durs) / len(durs):.1f} us (warm-up included).")
+        lines.append(f"Grouped GEMM (`{pattern.pattern}`), {which}: {len(durs)} launches, "
+                     f"mean {sum(durs) / len(durs):.1f} us.")
     if bench is not None:
         g = bench["roofline"] if kernel == "bf16" else bench["mxfp8"]["grouped_gemm"]
         lines.append(f"bench.py's event-timed mean launch over its timed steps in the same run: "
@@ -234,6 +243,8 @@ def main():
     st.add_argument("--command", required=True, help="the command that produced the run")
     st.add_argument("--note", default="")
     st.add_argument("--kernel", choices=sorted(KERNELS), default="bf16")
+    st.add_argument("--window", default=None, metavar="START:COUNT",
+                    help="only these matching dispatches, in dispatch order")
     st.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "traffic":
@@ -241,7 +252,9 @@ def main():
     elif a.cmd == "hbm":
         hbm(a.fetch, a.write, a.copy_bytes, a.title, a.command, a.out)
     elif a.cmd == "stats":
-        stats(a.stats, a.trace, a.bench_log, a.title, a.command, a.note, a.out, a.kernel)
+        win = tuple(int(v) for v in a.window.split(":")) if a.window else None
+        stats(a.stats, a.trace, a.bench_log, a.title, a.command, a.note, a.out, a.kernel,
+              window=win)
     else:
         mfma(a.csv, a.title, a.command, a.out)
 
