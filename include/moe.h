@@ -139,11 +139,27 @@ size_t moe_workspace_size(const moe_shape* s);
  *                    of the z row.
  *   ws               workspace; receives per-block expert histograms, in-block
  *                    ranks and per-block softmax column sums.
- * Logits must be finite (not checked).
+ * Logits must be finite (not checked here; moe_count_nonfinite checks them).
  */
 moe_status moe_route(const moe_shape* s, const void* x, const void* w_router,
                      const float* b_router, float* logits, int32_t* topk_ids,
                      float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_count_nonfinite - a debugging aid for moe_route's precondition: writes
+ * to *count the number of non-finite values (NaN, +inf, -inf) among the T*E
+ * fp32 logits.  One workgroup counts in a fixed order, so the result is exact
+ * and deterministic; call it between moe_route and moe_permute, on the same
+ * stream, when inputs may hold NaN or infinities.
+ *
+ *   logits   [T,E]   fp32: what moe_route wrote (or the caller's logits with
+ *                    MOE_FLAG_LOGITS_IN)
+ *   count    [1]     int64 out (device)
+ * Errors: the shape checks of moe_check_shape; MOE_ERR_INVALID_ARG for a NULL
+ * pointer.
+ */
+moe_status moe_count_nonfinite(const moe_shape* s, const float* logits, int64_t* count,
+                               void* stream);
 
 /*
  * moe_aux_loss - aux = E * sum_e f_e * P_e ([comm] 3.2), f_e = count_e/(T*K)

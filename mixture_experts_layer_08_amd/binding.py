@@ -29,7 +29,7 @@ MOE_FLAG_GUMBEL = 4
 # Every symbol include/moe.h declares.
 EXPORTS = (
     "moe_status_string", "moe_check_shape", "moe_capacity", "moe_max_rows",
-    "moe_workspace_size", "moe_route", "moe_aux_loss", "moe_permute",
+    "moe_workspace_size", "moe_route", "moe_count_nonfinite", "moe_aux_loss", "moe_permute",
     "moe_expert_ffn", "moe_combine", "moe_combine_backward", "moe_route_backward",
     "moe_expert_ffn_backward", "moe_permute_backward", "moe_mx_operand_scale_bytes",
     "moe_quantize_weights_mxfp8", "moe_permute_mxfp8", "moe_expert_ffn_mxfp8",
@@ -92,6 +92,8 @@ def lib():
         L.moe_workspace_size.argtypes = [_SHAPE]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_count_nonfinite.restype = ctypes.c_int
+        L.moe_count_nonfinite.argtypes = [_SHAPE, _P, _P, _P]
         L.moe_aux_loss.restype = ctypes.c_int
         L.moe_aux_loss.argtypes = [_SHAPE, _P, _SZ, _P, _P]
         L.moe_permute.restype = ctypes.c_int
@@ -174,6 +176,11 @@ def moe_route(s, x, w_router, b_router, logits, topk_ids, topk_w, ws, stream=Non
     _check("moe_route", lib().moe_route(
         ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(logits),
         _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_count_nonfinite(s, logits, count, stream=None):
+    _check("moe_count_nonfinite", lib().moe_count_nonfinite(
+        ctypes.byref(s), _ptr(logits), _ptr(count), _stream(stream)))
 
 
 def moe_aux_loss(s, ws, aux, stream=None):

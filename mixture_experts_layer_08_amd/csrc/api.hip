@@ -274,6 +274,15 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_router,
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
+moe_status moe_count_nonfinite(const moe_shape* s, const float* logits, int64_t* count,
+                               void* stream) {
+  const moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!logits || !count) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_count_nonfinite(logits, (size_t)s->T * (size_t)s->E,
+                                           (long long*)count, (hipStream_t)stream));
+}
+
 moe_status moe_aux_loss(const moe_shape* s, const void* ws, size_t ws_bytes, float* aux,
                         void* stream) {
   moe_status st = moe_check_shape(s);

@@ -46,6 +46,7 @@ struct RouteArgs {
 size_t route_lds_bytes(int E);
 int route_col_tiles(int E);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_count_nonfinite(const float* v, size_t n, long long* count, hipStream_t st);
 
 struct PermuteArgs {
   bool bf16;

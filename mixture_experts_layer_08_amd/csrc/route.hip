@@ -380,6 +380,29 @@ __global__ __launch_bounds__(256) void k_route_from_logits(
                  hist, psum, lrank);
 }
 
+// Number of non-finite values among n fp32 values, by one workgroup of 1024
+// threads in a fixed order (64-bit counts, exact and deterministic).
+__global__ __launch_bounds__(1024) void k_count_nonfinite(const float* __restrict__ v, size_t n,
+                                                          long long* __restrict__ count) {
+  __shared__ long long s_part[16];
+  long long c = 0;
+  for (size_t i = threadIdx.x; i < n; i += 1024) c += isfinite(v[i]) ? 0 : 1;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, kWave);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long t = 0;
+    for (int w = 0; w < 16; ++w) t += s_part[w];
+    *count = t;
+  }
+}
+
+hipError_t launch_count_nonfinite(const float* v, size_t n, long long* count, hipStream_t st) {
+  k_count_nonfinite<<<1, 1024, 0, st>>>(v, n, count);
+  return hipGetLastError();
+}
+
 size_t route_lds_bytes(int E) { return (size_t)kRouteBlock * (E | 1) * sizeof(float); }
 
 // bf16 router: the two weight buffers or the fp32 logits tile, whichever is

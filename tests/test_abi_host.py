@@ -157,6 +157,13 @@ def _call_route(lib, s, ws_ptr=0x1000, ws_bytes=1 << 30, ptr=0x2000):
     return lib.moe_route(ctypes.byref(s), ptr, ptr, None, ptr, ptr, ptr, ws_ptr, ws_bytes, None)
 
 
+def test_count_nonfinite_rejects_bad_arguments(lib):
+    assert lib.moe_count_nonfinite(ctypes.byref(shape()), None, 0x2000, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_count_nonfinite(ctypes.byref(shape()), 0x2000, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_count_nonfinite(ctypes.byref(shape(E=0)), 0x2000, 0x2000, None) == \
+        B.MOE_ERR_INVALID_ARG
+
+
 def test_route_rejects_bad_arguments_before_launch(lib):
     s = shape()
     # null outputs
