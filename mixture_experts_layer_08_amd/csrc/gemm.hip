@@ -326,27 +326,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 
   // Epilogue straight from registers: lane owns row m of each 32x32 tile and
-  // four runs of 4 consecutive columns.
+  // four runs of 4 consecutive columns, 8 g + 4 kh .. +3 (g = 0..3).  Lanes m
+  // and m + 32 hold the two halves of every 8-column group, so one exchange
+  // of a 4-value half per pair of groups gives each lane 8 consecutive
+  // columns: lane kh = 0 stores columns 16 p .. 16 p + 7, kh = 1 columns
+  // 16 p + 8 .. 16 p + 15, one 16-byte store each (the weight-gradient form
+  // stores its fp32 groups of 4 directly).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = wm * 128 + i * 32 + rr;
-    if (m >= rows) continue;
+    if (m >= rows) continue;  // uniform over the lane pair (m, m + 32)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      if (kTN) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * kh;
-        if (n < N) {
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * kh;
+          if (n < N) {
+            float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
+            *(f32x4*)(crow + n) = f32x4{acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                                        acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+        }
+        continue;
+      }
+      bf16* crow = (bf16*)Cv;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int nb = n0 + wn * 64 + j * 32 + 16 * p;  // first column of the pair
+        u32x2 d[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int g = 2 * p + h;
+          const bool ok = nb + 8 * h < N;  // whole 8-column group in or out (N % 8 == 0)
+          const size_t at = (size_t)(row0 + m) * N + nb + 8 * h + 4 * kh;
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (kTN) {
-            float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
-            *(f32x4*)(crow + n) = f32x4{v0, v1, v2, v3};
-            continue;
-          }
-          const size_t at = (size_t)(row0 + m) * N + n;
-          bf16* crow = (bf16*)Cv;
-          if (EPI == kEpiGeluSave)
+          if (EPI == kEpiGeluSave && ok)
             *(u32x2*)(Ep + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
           if (EPI == kEpiGelu || EPI == kEpiGeluSave) {
             v0 = gelu_tanh_f32(v0);
@@ -354,20 +370,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
             v2 = gelu_tanh_f32(v2);
             v3 = gelu_tanh_f32(v3);
           } else if (EPI == kEpiGeluGrad) {
-            const u32x2 u = *(const u32x2*)(Ep + at);
+            const u32x2 u = ok ? *(const u32x2*)(Ep + at) : u32x2{0u, 0u};
             v0 *= gelu_tanh_grad_f32(bf16_lo(u[0]));
             v1 *= gelu_tanh_grad_f32(bf16_hi(u[0]));
             v2 *= gelu_tanh_grad_f32(bf16_lo(u[1]));
             v3 *= gelu_tanh_grad_f32(bf16_hi(u[1]));
           } else if (EPI == kEpiAccum) {
-            const u32x2 c = *(const u32x2*)(crow + at);
+            const u32x2 c = ok ? *(const u32x2*)(crow + at) : u32x2{0u, 0u};
             v0 += bf16_lo(c[0]);
             v1 += bf16_hi(c[0]);
             v2 += bf16_lo(c[1]);
             v3 += bf16_hi(c[1]);
           }
-          *(u32x2*)(crow + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          d[h] = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
+        // kh = 0 needs its partner's first group, kh = 1 its partner's second
+        const u32x2 send = kh ? d[0] : d[1];
+        const uint32_t x0 = (uint32_t)__shfl_xor((int)send[0], 32, kWave);
+        const uint32_t x1 = (uint32_t)__shfl_xor((int)send[1], 32, kWave);
+        const u32x4 o = kh ? u32x4{x0, x1, d[1][0], d[1][1]} : u32x4{d[0][0], d[0][1], x0, x1};
+        const int c0 = nb + 8 * kh;
+        if (c0 < N) *(u32x4*)(crow + (size_t)(row0 + m) * N + c0) = o;
       }
     }
   }
