@@ -249,8 +249,22 @@ __global__ __launch_bounds__(256) void k_route_bf16(
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (size_t)t0 * H), (short)0, nt * H * 2, kBufferFormat);
   const uint32_t xoff = (uint32_t)((wave * 16 + (lane & 15)) * H + kg) * 2;
+  // Each workgroup walks the K range in its own rotated order: the chunks
+  // start at chunk rc, and the steps inside every chunk at step ri (the sum
+  // over k does not depend on the order).  Workgroups running side by side
+  // then read different column offsets of their rows, rather than all
+  // hitting the same offsets of rows 512 KiB apart at once, which measured
+  // ~20% faster on cold x.
+  const int rot = (int)((blockIdx.x * 37u) % (unsigned)(nchunks * SPC));
+  const int rc = rot / SPC, ri = rot % SPC;
+  auto kstep = [&](int s) {  // sequence step -> K-step (SPC is a power of two)
+    const int c = s / SPC;
+    return ((c + rc) % nchunks) * SPC + (((s % SPC) + ri) & (SPC - 1));
+  };
   auto xload = [&](int s) -> bf16x8 {
-    const uint32_t off = s * 32 + kg < H ? xoff + (uint32_t)s * 64 : kOffsetOob;
+    const int ks = kstep(s);
+    const uint32_t off =
+        s < nchunks * SPC && ks * 32 + kg < H ? xoff + (uint32_t)ks * 64 : kOffsetOob;
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
   };
   // weight chunk c: thread's vectors v = tid + 256 q -> row v / (KC/8),
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(256) void k_route_bf16(
     for (int q = 0; q < WPT; ++q) {
       const int v = tid + 256 * q;
       const int r = v / (KC / 8), p = v % (KC / 8);
-      const int k = c * KC + p * 8;
+      const int k = ((c + rc) % nchunks) * KC + p * 8;
       const uint32_t off = k < H ? (uint32_t)(r * H + k) * 2 : kOffsetOob;
       wreg[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
     }
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(256) void k_route_bf16(
       // steps past the last chunk read the last chunk's buffer (finite
       // weights times zero rows of x): the other buffer may never have been
       // written, and stale LDS bits could be NaN
-      const bf16* wb = wbuf + (min(c, nchunks - 1) & 1) * WBUF + (i % SPC) * 32 + b_off;
+      const bf16* wb = wbuf + (min(c, nchunks - 1) & 1) * WBUF + (((i % SPC) + ri) & (SPC - 1)) * 32 + b_off;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const bf16x8 b = *(const bf16x8*)(wb + ct * 16 * WROW);
