@@ -190,7 +190,9 @@ def forward_mxfp8(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, K: int, cf: float,
     Routing is the float oracle's, from the unquantised x (or from the given
     float32 ``logits``).  Dispatch carries mx_quantize(x) rows; every expert
     runs :func:`ffn_mxfp8` with its quantised weights; combine weights the
-    dequantised FP8 outputs by the routing weights in float64.
+    dequantised FP8 outputs by the routing weights in float64.  Besides the
+    codes and scales, ``h`` (and ``sh_h``) hold the GELU outputs before
+    quantisation, float64, packed rows.
     """
     E = w1.shape[0]
     l_own = O.router_logits(x, w_r, b_r)
@@ -207,6 +209,7 @@ def forward_mxfp8(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, K: int, cf: float,
     offsets = r["offsets"]
     N = int(offsets[-1])
     H, h = x.shape[1], w1.shape[2]
+    h_val = np.zeros((N, h), np.float64)
     h_codes = np.zeros((N, h), np.uint8)
     h_scales = np.zeros((N, h // BLOCK), np.uint8)
     o_codes = np.zeros((N, H), np.uint8)
@@ -216,6 +219,7 @@ def forward_mxfp8(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, K: int, cf: float,
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
             f = ffn_mxfp8(x_d[token_of[a:b]], w1d[e], w2d[e])
+            h_val[a:b] = f["h"]
             h_codes[a:b], h_scales[a:b] = f["h_codes"], f["h_scales"]
             o_codes[a:b], o_scales[a:b] = f["o_codes"], f["o_scales"]
             out[a:b] = f["out"]
@@ -225,10 +229,10 @@ def forward_mxfp8(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, K: int, cf: float,
         s2c, s2s = mx_quantize(ws2, axis=0)
         fs = ffn_mxfp8(x_d, mx_dequantize(s1c, s1s, axis=0), mx_dequantize(s2c, s2s, axis=0))
         shared = fs["out"]
-        r.update(sh_h_codes=fs["h_codes"], sh_h_scales=fs["h_scales"],
+        r.update(sh_h=fs["h"], sh_h_codes=fs["h_codes"], sh_h_scales=fs["h_scales"],
                  sh_codes=fs["o_codes"], sh_scales=fs["o_scales"])
     y = O.combine(out, r["row_of"], r["w"], shared)
     r.update(x_codes=x_codes, x_scales=x_scales, w1_codes=w1c, w1_scales=w1s,
-             w2_codes=w2c, w2_scales=w2s, h_codes=h_codes, h_scales=h_scales,
+             w2_codes=w2c, w2_scales=w2s, h=h_val, h_codes=h_codes, h_scales=h_scales,
              o_codes=o_codes, o_scales=o_scales, out=out, shared=shared, y=y)
     return r
