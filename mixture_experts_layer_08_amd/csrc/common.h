@@ -5,7 +5,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
+
+// Host side: a kernel that takes more than 64 KiB of dynamic LDS must be
+// allowed to, per device (the attribute belongs to the device's copy of the
+// kernel).  allow_dynamic_lds<kernel>() raises the kernel's cap to the
+// device's LDS per workgroup (160 KiB on gfx950) less the kernel's static
+// LDS, the first time it runs on each of the first 64 devices (every time on
+// others).  Concurrent first calls both set the same value.
+template <auto kKernel>
+hipError_t allow_dynamic_lds() {
+  static std::atomic<unsigned long long> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  int lds_per_block = 0;
+  e = hipDeviceGetAttribute(&lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  hipFuncAttributes fa;
+  e = hipFuncGetAttributes(&fa, (const void*)kKernel);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)kKernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lds_per_block - (int)fa.sharedSizeBytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

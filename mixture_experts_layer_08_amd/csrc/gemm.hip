@@ -494,14 +494,8 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
 
 template <int LAYOUT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
-  static bool lds_ok = false;
-  if (!lds_ok) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_bf16<LAYOUT, EPI>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kSmem2);
-    if (e != hipSuccess) return e;
-    lds_ok = true;
-  }
+  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_bf16<LAYOUT, EPI>>();
+  if (e != hipSuccess) return e;
   const int ntc = (a.N + BN2 - 1) / BN2;
   int mtb = 0;
   long long grid;

@@ -304,14 +304,8 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
 
 template <int EPI>
 static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
-  static bool lds_ok = false;
-  if (!lds_ok) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_grouped_gemm_mx8<EPI>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kMxSmem);
-    if (e != hipSuccess) return e;
-    lds_ok = true;
-  }
+  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_mx8<EPI>>();
+  if (e != hipSuccess) return e;
   if (a.Kd <= 0 || a.Kd % kMxBK != 0 || a.N <= 0 || a.N % kMxBlock != 0) return hipErrorInvalidValue;
   const int ntc = (a.N + kMxBN - 1) / kMxBN;
   const int mtb = a.offsets ? (a.max_rows + kMxBM - 1) / kMxBM + a.G

@@ -434,20 +434,13 @@ int route_col_tiles(int E) {
   return ct <= 1 ? 1 : ct <= 2 ? 2 : ct <= 4 ? 4 : ct <= 8 ? 8 : 16;
 }
 
-// Dynamic LDS above 64 KiB must be allowed explicitly; gfx950 has 160 KiB of
-// LDS per workgroup.
-template <typename F>
-static hipError_t allow_lds(F* kernel, size_t bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
-}
-
 template <int CT>
 static hipError_t launch_route_bf16(const RouteArgs& a, int nblk, hipStream_t st) {
   const size_t lds = route_bf16_lds_bytes<CT>(a.E);
-  hipError_t err = allow_lds(k_route_bf16<CT>, lds);
-  if (err != hipSuccess) return err;
+  if (lds > 65536) {
+    const hipError_t err = allow_dynamic_lds<k_route_bf16<CT>>();
+    if (err != hipSuccess) return err;
+  }
   k_route_bf16<CT><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.wT, a.bias, a.logits,
                                            a.topk_ids, a.topk_w, a.hist, a.psum, a.lrank, a.T,
                                            a.H, a.E, a.K, nblk, a.noise);
@@ -459,13 +452,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const size_t lds = route_lds_bytes(a.E);
   hipError_t err;
   if (a.logits_in) {
-    if ((err = allow_lds(k_route_from_logits, lds)) != hipSuccess) return err;
+    if (lds > 65536 && (err = allow_dynamic_lds<k_route_from_logits>()) != hipSuccess) return err;
     k_route_from_logits<<<nblk, 256, lds, st>>>(a.logits, a.topk_ids, a.topk_w, a.hist, a.psum,
                                                 a.lrank, a.T, a.E, a.K, nblk);
     return hipGetLastError();
   }
   if (!a.bf16) {
-    if ((err = allow_lds(k_route_f32, lds)) != hipSuccess) return err;
+    if (lds > 65536 && (err = allow_dynamic_lds<k_route_f32>()) != hipSuccess) return err;
     k_route_f32<<<nblk, 256, lds, st>>>((const float*)a.x, (const float*)a.w_r, a.bias,
                                         a.logits, a.topk_ids, a.topk_w, a.hist, a.psum,
                                         a.lrank, a.T, a.H, a.E, a.K, nblk, a.noise);
