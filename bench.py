@@ -308,8 +308,8 @@ def backward_leg(w, p, dev, steps: int, warmup: int, alpha: float) -> dict:
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported by this build "
-              f"(the layer forward runs on a single GPU's token batch).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the layer forward runs on one GPU's token "
+              f"batch and has no multi-GPU path, so --gpus {a.gpus} is refused.", file=sys.stderr)
         sys.exit(2)
 
     import torch
