@@ -270,12 +270,25 @@ moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_o
 size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols);
 
 /*
+ * Bytes of the weight codes moe_quantize_weights_mxfp8 writes for `batch`
+ * [K,N] weights: batch * ceil(N/256) * 256 * K (0 if an argument is < 1).
+ */
+size_t moe_mx_weight_code_bytes(int32_t batch, int32_t K, int32_t N);
+
+/*
  * moe_quantize_weights_mxfp8 - expert weights to MXFP8, once, outside the
  * forward ([comm] 4.2).
  *
  *   w       [batch,K,N]  weights (dtype MOE_BF16 or MOE_F32), K the
  *                        contraction dimension (H for W1, h for W2)
- *   q       [batch,N,K]  out: E4M3 codes, transposed so K is contiguous
+ *   q       out: E4M3 codes of the transposed [batch,N,K] weights in panels
+ *           of 256 rows x 64 codes, moe_mx_weight_code_bytes(batch, K, N)
+ *           bytes: code (b, n, k) lies at byte
+ *             ((b*P + n/256) * (K/64) + k/64) * 16384 + (n%256) * 64 + k%64,
+ *           P = ceil(N/256), so one 64-value K-step of a 256-row GEMM tile
+ *           is 16 contiguous KiB.  Rows n >= N of each slice's last panel
+ *           are padding: never written, and read only into GEMM output
+ *           columns that are never stored.
  *   scales  [batch,ceil(K/128),N,4]  out: operand layout of each [N,K] slice
  * K must be a multiple of 64 and N of 32 (MOE_ERR_UNSUPPORTED), N*K < 2^31.
  */

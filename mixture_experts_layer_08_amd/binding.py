@@ -32,6 +32,7 @@ EXPORTS = (
     "moe_workspace_size", "moe_route", "moe_count_nonfinite", "moe_aux_loss", "moe_permute",
     "moe_expert_ffn", "moe_combine", "moe_combine_backward", "moe_route_backward",
     "moe_expert_ffn_backward", "moe_permute_backward", "moe_mx_operand_scale_bytes",
+    "moe_mx_weight_code_bytes",
     "moe_quantize_weights_mxfp8", "moe_permute_mxfp8", "moe_expert_ffn_mxfp8",
     "moe_combine_mxfp8",
 )
@@ -113,6 +114,8 @@ def lib():
         L.moe_permute_backward.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_mx_operand_scale_bytes.restype = _SZ
         L.moe_mx_operand_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.moe_mx_weight_code_bytes.restype = _SZ
+        L.moe_mx_weight_code_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.moe_quantize_weights_mxfp8.restype = ctypes.c_int
         L.moe_quantize_weights_mxfp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
@@ -241,6 +244,10 @@ def moe_permute_backward(s, d_xp, row_of, d_x_shared, d_logits, w_router, dx, ws
 
 def moe_mx_operand_scale_bytes(rows: int, cols: int) -> int:
     return lib().moe_mx_operand_scale_bytes(int(rows), int(cols))
+
+
+def moe_mx_weight_code_bytes(batch: int, K: int, N: int) -> int:
+    return lib().moe_mx_weight_code_bytes(int(batch), int(K), int(N))
 
 
 def moe_quantize_weights_mxfp8(w, dtype, batch, K, N, q, scales, stream=None):

@@ -567,6 +567,11 @@ size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols) {
   return mx_operand_scale_bytes(rows, cols);
 }
 
+size_t moe_mx_weight_code_bytes(int32_t batch, int32_t K, int32_t N) {
+  if (batch < 1 || K < 1 || N < 1) return 0;
+  return mx_weight_code_bytes(batch, K, N);
+}
+
 moe_status moe_quantize_weights_mxfp8(const void* w, int32_t dtype, int32_t batch, int32_t K,
                                       int32_t N, uint8_t* q, uint8_t* scales, void* stream) {
   if (!w || !q || !scales) return MOE_ERR_INVALID_ARG;

@@ -51,6 +51,7 @@ constexpr uint32_t kMxScaleBytes = (kMxBM + kMxBN) * 4;        // 2 KiB
 constexpr uint32_t kMxStageBytes = kMxDataBytes + kMxScaleBytes;
 constexpr size_t kMxSmem = (size_t)kMxStages * kMxStageBytes;  // 136 KiB
 static_assert(kMxSmem <= 160 * 1024, "LDS ring exceeds 160 KiB");
+static_assert(kMxBN == kMxPanelRows && kMxBK == kMxPanelK, "a B K-step is one weight panel");
 static_assert(kMxStages == 4, "the wait counts below assume four stages");
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -79,8 +80,9 @@ __device__ __forceinline__ f32x16 mfma_mx8(const i32x8& b, const i32x8& a, const
 // operand layout with leading dimension c_ld (the next GEMM's A operand).
 //
 // A: [a_rows][Kd] codes, As operand layout (leading dimension a_ld);
-// B: [G][N][Kd] codes, Bs [G][ceil(Kd/128)][N][4].  Kd is a multiple of 64 and
-// N of 32.  Rows of a tile past its segment are computed from whatever the
+// B: [G][N][Kd] codes in 256 x 64-byte panels (mx.h), so that one K-step of a
+// tile's B operand is 16 contiguous KiB; Bs [G][ceil(Kd/128)][N][4].  Kd is a
+// multiple of 64 and N of 32.  Rows of a tile past its segment are computed from whatever the
 // buffers hold there (even NaN) and never stored; each output row depends on
 // its own A row only.
 template <int EPI>
@@ -114,7 +116,10 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
   const int r_row_l = lane >> 2;
   const int r_chunk = mx_swz(r_row_l, lane & 3);
   const u32x4 ra = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd);
-  const u32x4 rb = make_rsrc_words(B + ((size_t)seg * N + n0) * Kd, (long long)(N - n0) * Kd);
+  // B: this tile's panels, one per K-step (rows past N are panel padding)
+  const u32x4 rb = make_rsrc_words(B + ((size_t)seg * nt_count + nt) * kMxBN * (size_t)Kd,
+                                   (long long)kMxBN * Kd);
+  const uint32_t b_off = (uint32_t)((r_row_l + 16 * wave) * kMxBK + r_chunk * 16);
   const uint32_t d_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 16);
   const uint32_t d_stride = (uint32_t)(8 * 16 * Kd);
   // scales: waves 0-3 load A rows 64 w .. +63, waves 4-7 B rows 64 (w-4) ..
@@ -139,7 +144,9 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
                  in_k ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
     } else if (d < 2 * kMxDma) {
       dma_load16(st + kMxBM * kMxBK + (8 * (d - kMxDma) + wave) * 1024,
-                 in_k ? d_off + (d - kMxDma) * d_stride + (uint32_t)kt * kMxBK : kOob, rb);
+                 in_k ? b_off + (d - kMxDma) * (8 * 16 * kMxBK) + (uint32_t)kt * (kMxBN * kMxBK)
+                      : kOob,
+                 rb);
     } else {
       dma_load4(st + s_lds, in_k ? s_base + (uint32_t)(kt >> 1) * s_slab : kOob, rs);
     }

@@ -36,6 +36,25 @@ __host__ __device__ inline size_t mx_operand_scale_index(long long ld, long long
   return ((size_t)(blk >> 2) * (size_t)ld + (size_t)r) * 4 + (size_t)(blk & 3);
 }
 
+// Weight codes in panels: for a [G][N][K] operand (K the contraction), the
+// 256 x 64-byte block of rows 256 t .. 256 t + 255 and columns 64 j .. 64 j + 63
+// of slice g is one contiguous 16 KiB panel, panels ordered (g, t, j):
+//   code (g, n, k) at ((g * T + n / 256) * (K / 64) + k / 64) * 16384
+//                     + (n % 256) * 64 + k % 64,   T = ceil(N / 256).
+// One K-step of a GEMM tile's B operand is then one panel.  Rows n >= N of a
+// slice's last panel are padding.
+constexpr int kMxPanelRows = 256, kMxPanelK = 64;
+__host__ __device__ inline size_t mx_weight_code_bytes(long long G, long long K, long long N) {
+  return (size_t)G * (size_t)((N + kMxPanelRows - 1) / kMxPanelRows) * kMxPanelRows * (size_t)K;
+}
+__host__ __device__ inline size_t mx_weight_code_offset(long long g, long long n, long long k,
+                                                        long long K, long long N) {
+  const long long T = (N + kMxPanelRows - 1) / kMxPanelRows;
+  return (size_t)(((g * T + n / kMxPanelRows) * (K / kMxPanelK) + k / kMxPanelK) *
+                      (kMxPanelRows * kMxPanelK) +
+                  (n % kMxPanelRows) * kMxPanelK + k % kMxPanelK);
+}
+
 // Scale code of a block from its float32 absolute maximum.
 __device__ __forceinline__ uint32_t mx_scale_code(float amax) {
   const int f = (int)((__float_as_uint(amax) >> 23) & 0xffu);

@@ -10,7 +10,8 @@
 
 namespace moe {
 
-// w [G][Kd][N] (bf16 or fp32, row-major) -> q [G][N][Kd] E4M3 codes and
+// w [G][Kd][N] (bf16 or fp32, row-major) -> q: E4M3 codes of the transposed
+// [G][N][Kd] weights in 256 x 64-byte panels (mx.h), and
 // s [G][ceil(Kd/128)][N][4] block scales (operand layout with R = N): the
 // blocks run along Kd, the contraction dimension of the expert GEMM.  One
 // workgroup per (expert, 128-row slab of Kd, 64 columns): the tile is staged
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void k_quantize_weight_mx8(const void* __restr
   for (int i = 0; i < 8; ++i)
     c[i] = mx_encode4(tile[32 * b + 4 * i][nn], tile[32 * b + 4 * i + 1][nn],
                       tile[32 * b + 4 * i + 2][nn], tile[32 * b + 4 * i + 3][nn], inv);
-  u32x4* dst = (u32x4*)(q + ((size_t)g * N + n) * Kd + kb);
+  u32x4* dst = (u32x4*)(q + mx_weight_code_offset(g, n, kb, Kd, N));  // 32 bytes in one panel row
   dst[0] = u32x4{c[0], c[1], c[2], c[3]};
   dst[1] = u32x4{c[4], c[5], c[6], c[7]};
   s[(((size_t)g * nslab + slab) * N + n) * 4 + b] = (uint8_t)code;

@@ -201,8 +201,9 @@ def backward(buf: MoeBuffers, g: GradBuffers, p: dict, dy, alpha: float = 0.0,
 
 @dataclasses.dataclass
 class MxWeights:
-    """Expert weights in MXFP8 (moe_quantize_weights_mxfp8): codes [E,N,K]
-    with K the contraction dimension, operand-layout scales."""
+    """Expert weights in MXFP8 (moe_quantize_weights_mxfp8): codes of the
+    [E,N,K] transposed weights (K the contraction dimension) in 256 x 64
+    panels, flat uint8 of moe_mx_weight_code_bytes; operand-layout scales."""
     w1_q: torch.Tensor
     w1_s: torch.Tensor
     w2_q: torch.Tensor
@@ -218,7 +219,8 @@ class MxWeights:
         dt = B.MOE_BF16 if p["w1"].dtype == torch.bfloat16 else B.MOE_F32
 
         def q(t, G, K, N):
-            codes = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+            codes = torch.empty((B.moe_mx_weight_code_bytes(G, K, N),), dtype=torch.uint8,
+                                device=dev)
             sc = torch.empty((G * B.moe_mx_operand_scale_bytes(N, K),), dtype=torch.uint8,
                              device=dev)
             B.moe_quantize_weights_mxfp8(t, dt, G, K, N, codes, sc, stream)

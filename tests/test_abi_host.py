@@ -288,3 +288,9 @@ def test_mxfp8_calls_reject_bad_arguments_before_launch(lib):
     assert lib.moe_quantize_weights_mxfp8(*q(128, 64, w=None)) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_mx_operand_scale_bytes(100, 192) == 2 * 100 * 4
     assert lib.moe_mx_operand_scale_bytes(7, 128) == 7 * 4
+    # weight codes in 256-row panels: rows padded per slice
+    assert lib.moe_mx_weight_code_bytes(8, 4096, 14336) == 8 * 14336 * 4096
+    assert lib.moe_mx_weight_code_bytes(3, 192, 96) == 3 * 256 * 192
+    assert lib.moe_mx_weight_code_bytes(2, 64, 288) == 2 * 512 * 64
+    assert lib.moe_mx_weight_code_bytes(0, 64, 32) == 0
+    assert lib.moe_mx_weight_code_bytes(1, 64, 0) == 0

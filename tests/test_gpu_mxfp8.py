@@ -68,6 +68,25 @@ def u8(t):
     return t.detach().cpu().numpy()
 
 
+def unpanel(flat, G, K, N):
+    """moe_quantize_weights_mxfp8's panel layout -> codes [G][N][K] (numpy):
+    panels of 256 rows x 64 codes ordered (g, row block, K block)."""
+    P = (N + 255) // 256
+    a = u8(flat)[: G * P * 256 * K].reshape(G, P, K // 64, 256, 64)
+    return a.transpose(0, 1, 3, 2, 4).reshape(G, P * 256, K)[:, :N, :]
+
+
+def panel_rows(flat, G, K, N, cols):
+    """Codes [G][len(cols)][K] of the given weight columns (rows of the
+    transposed weights), gathered on the device by the panel formula."""
+    P = (N + 255) // 256
+    g = torch.arange(G, device=flat.device)[:, None, None]
+    n = torch.as_tensor(cols, device=flat.device)[None, :, None]
+    k = torch.arange(K, device=flat.device)[None, None, :]
+    idx = ((g * P + n // 256) * (K // 64) + k // 64) * 16384 + (n % 256) * 64 + k % 64
+    return u8(torch.take(flat, idx))
+
+
 def op_rows(flat, R, Kd):
     """Operand-layout scales [ceil(Kd/128)][R][4] -> row layout [R][Kd/32]."""
     ns = (Kd + 127) // 128
@@ -270,12 +289,18 @@ def test_quantize_weights_bit_exact(dtype, G, K, N):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     w = w.to(tdt)
     dev = w.to("cuda")
-    q = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    nbytes = B.moe_mx_weight_code_bytes(G, K, N)
+    assert nbytes == G * ((N + 255) // 256) * 256 * K
+    q = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
     s = torch.empty((G * B.moe_mx_operand_scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
     B.moe_quantize_weights_mxfp8(dev, B.MOE_BF16 if dtype == "bf16" else B.MOE_F32, G, K, N, q, s)
     torch.cuda.synchronize()
     rc, rs = M.quantize_weights(w.to(torch.float32).numpy())
-    assert np.array_equal(u8(q), rc.transpose(0, 2, 1))
+    assert np.array_equal(unpanel(q, G, K, N), rc.transpose(0, 2, 1))
+    # the padding rows of each slice's last panel are left as they were
+    P = (N + 255) // 256
+    full = u8(q).reshape(G, P, K // 64, 256, 64).transpose(0, 1, 3, 2, 4).reshape(G, P * 256, K)
+    assert np.all(full[:, N:, :] == 0xA5)
     per = B.moe_mx_operand_scale_bytes(N, K)
     for e in range(G):
         assert np.array_equal(op_rows(s[e * per:(e + 1) * per], N, K), rs[e].T), f"scales {e}"
@@ -384,7 +409,7 @@ def test_mixtral_full_size_sampled():
     cols = np.array([0, 1, 5000, 14335])
     w1c = np32(p["w1"][:, :, torch.as_tensor(cols, device="cuda")])
     rc, rs = M.quantize_weights(w1c)
-    gq = u8(mw.w1_q[:, torch.as_tensor(cols, device="cuda"), :])
+    gq = panel_rows(mw.w1_q, w.E, w.H, w.h, cols)
     assert np.array_equal(gq, rc.transpose(0, 2, 1))
     say("  W1 codes of sampled columns bit-exact")
     off = r["offsets"]
