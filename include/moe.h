@@ -266,12 +266,14 @@ moe_status moe_combine(const moe_shape* s, const void* out, const int32_t* row_o
  * aligned, scale pointers 4-byte aligned.
  */
 
-/* Bytes of an operand-layout scale tensor for `rows` x `cols` values. */
+/* Bytes of an operand-layout scale tensor for `rows` x `cols` values (0 for
+ * negative arguments or a size that does not fit in size_t). */
 size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols);
 
 /*
  * Bytes of the weight codes moe_quantize_weights_mxfp8 writes for `batch`
- * [K,N] weights: batch * ceil(N/256) * 256 * K (0 if an argument is < 1).
+ * [K,N] weights: batch * ceil(N/256) * 256 * K (0 if an argument is < 1 or
+ * the size does not fit in size_t).
  */
 size_t moe_mx_weight_code_bytes(int32_t batch, int32_t K, int32_t N);
 

@@ -564,12 +564,21 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
 
 size_t moe_mx_operand_scale_bytes(int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return 0;
-  return mx_operand_scale_bytes(rows, cols);
+  size_t n;
+  if (__builtin_mul_overflow((uint64_t)((cols + 127) / 128), (uint64_t)rows, &n) ||
+      __builtin_mul_overflow(n, (size_t)4, &n))
+    return 0;
+  return n;
 }
 
 size_t moe_mx_weight_code_bytes(int32_t batch, int32_t K, int32_t N) {
   if (batch < 1 || K < 1 || N < 1) return 0;
-  return mx_weight_code_bytes(batch, K, N);
+  const uint64_t rows = ((uint64_t)N + kMxPanelRows - 1) / kMxPanelRows * kMxPanelRows;
+  size_t n;
+  if (__builtin_mul_overflow(rows, (uint64_t)K, &n) ||
+      __builtin_mul_overflow(n, (uint64_t)batch, &n))
+    return 0;
+  return n;
 }
 
 moe_status moe_quantize_weights_mxfp8(const void* w, int32_t dtype, int32_t batch, int32_t K,

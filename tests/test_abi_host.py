@@ -294,3 +294,7 @@ def test_mxfp8_calls_reject_bad_arguments_before_launch(lib):
     assert lib.moe_mx_weight_code_bytes(2, 64, 288) == 2 * 512 * 64
     assert lib.moe_mx_weight_code_bytes(0, 64, 32) == 0
     assert lib.moe_mx_weight_code_bytes(1, 64, 0) == 0
+    assert lib.moe_mx_weight_code_bytes(2 ** 31 - 1, 2 ** 31 - 64, 2 ** 31 - 32) == 0  # overflow
+    assert lib.moe_mx_weight_code_bytes(2 ** 20, 2 ** 20, 2 ** 20) == 2 ** 60
+    assert lib.moe_mx_operand_scale_bytes(2 ** 62, 2 ** 40) == 0  # overflow
+    assert lib.moe_mx_operand_scale_bytes(-1, 128) == 0
