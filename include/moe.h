@@ -40,6 +40,16 @@
  *   not overlap.
  * - Results are deterministic: no floating-point atomics, fixed reduction
  *   orders.
+ * - The per-block partial results of routing (expert histograms per block of
+ *   64 tokens, softmax column sums per block, in-block ranks) are an internal
+ *   format of the library, so they travel inside `ws` rather than as
+ *   arguments: moe_route writes them, moe_aux_loss and moe_permute read them.
+ *   moe_aux_loss runs before moe_permute and derives the per-expert counts
+ *   from those histograms itself.  One workspace serves every call of a
+ *   forward (and, with MOE_FLAG_TRAIN, of its backward), so
+ *   moe_workspace_size takes only the shape.
+ * - `stream` is a hipStream_t passed as void*, so that this header needs no
+ *   HIP include and a plain C caller can use it.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -53,10 +63,10 @@ extern "C" {
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer  */
-  MOE_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels support  */
-  MOE_ERR_WORKSPACE = 3,     /* ws_bytes below moe_workspace_size()         */
-  MOE_ERR_HIP = 4            /* a HIP launch or runtime call failed          */
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer  */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels support  */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_size()         */
+  MOE_ERR_HIP = -4           /* a HIP launch or runtime call failed          */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;

@@ -16,10 +16,10 @@ from typing import Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK = 0
-MOE_ERR_INVALID_ARG = 1
-MOE_ERR_UNSUPPORTED = 2
-MOE_ERR_WORKSPACE = 3
-MOE_ERR_HIP = 4
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_LOGITS_IN = 1

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -29,7 +30,16 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
+    # per-kernel register / scratch remarks, checked by check_resources()
+    "-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics",
 ]
+
+# Kernels whose LDS ring is kept in order by hand-counted `s_waitcnt vmcnt`
+# waits: those counts assume the LDS-direct loads are the only vector-memory
+# instructions in the K loop.  A register spill would add scratch loads and
+# stores to the count and release a wait before its stage has landed, so the
+# build refuses any scratch use or spill in them.
+NO_SCRATCH_KERNELS = ("k_grouped_gemm_bf16", "k_grouped_gemm_mx8")
 
 
 def hipcc() -> str:
@@ -39,25 +49,66 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmoe.so")
 
 
-def _compile(src: str) -> str:
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|"
+                     r"VGPRs|AGPRs|Occupancy \[waves/SIMD\]):\s*(\S+)")
+
+
+def resource_usage(remarks: str) -> dict:
+    """{kernel symbol: {field: value}} from hipcc's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = val
+    return out
+
+
+def check_resources(usage: dict) -> None:
+    """Refuse scratch or spills in the kernels of NO_SCRATCH_KERNELS."""
+    bad = []
+    for sym, f in usage.items():
+        if not any(k in sym for k in NO_SCRATCH_KERNELS):
+            continue
+        for key in ("ScratchSize [bytes/lane]", "VGPRs Spill", "SGPRs Spill"):
+            if f.get(key, "0") != "0":
+                bad.append(f"{sym}: {key} = {f[key]}")
+    if bad:
+        raise RuntimeError("kernels with hand-counted vmcnt waits must not use scratch:\n  "
+                           + "\n  ".join(bad))
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    # surface warnings other than hipcc's note about the host-side feature flag
-    noise = ("packed-fp32-ops", "not a recognized feature", "warning generated", "warnings generated")
+    # surface warnings other than hipcc's note about the host-side feature
+    # flag and the resource remarks
+    noise = ("packed-fp32-ops", "not a recognized feature", "warning generated",
+             "warnings generated", "kernel-resource-usage")
     msgs = [l for l in r.stderr.splitlines() if l.strip() and not any(n in l for n in noise)]
     if msgs:
         sys.stderr.write("\n".join(msgs) + "\n")
-    return obj
+    return obj, resource_usage(r.stderr)
 
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    usage = {k: v for _, u in results for k, v in u.items()}
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for sym in sorted(usage):
+            f.write(sym + " " + " ".join(f"{k}={v}" for k, v in usage[sym].items()) + "\n")
+    check_resources(usage)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -14,8 +14,11 @@ namespace moe {
 // kernel).  allow_dynamic_lds<kernel>() raises the kernel's cap to the
 // device's LDS per workgroup (160 KiB on gfx950) less the kernel's static
 // LDS, the first time it runs on each of the first 64 devices (every time on
-// others).  Concurrent first calls both set the same value.
-template <auto kKernel>
+// others).  Concurrent first calls both set the same value.  With kNoScratch
+// it also refuses (hipErrorInvalidDeviceFunction) a kernel whose code object
+// uses scratch memory: kernels that order their LDS ring with hand-counted
+// vmcnt waits would count a spill's scratch loads and stores too.
+template <auto kKernel, bool kNoScratch = false>
 hipError_t allow_dynamic_lds() {
   static std::atomic<unsigned long long> done{0};
   int dev = 0;
@@ -29,6 +32,7 @@ hipError_t allow_dynamic_lds() {
   hipFuncAttributes fa;
   e = hipFuncGetAttributes(&fa, (const void*)kKernel);
   if (e != hipSuccess) return e;
+  if (kNoScratch && fa.localSizeBytes != 0) return hipErrorInvalidDeviceFunction;
   e = hipFuncSetAttribute((const void*)kKernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           lds_per_block - (int)fa.sharedSizeBytes);
   if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);

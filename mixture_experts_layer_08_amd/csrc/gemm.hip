@@ -301,6 +301,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // iteration's barrier.  At the wait of iteration kt this wave has issued
   // steps up to kt+kStages-2, so allowing kStages-3 steps in flight means
   // step kt+1 has landed; after the barrier it has landed for every wave.
+  // These counts hold only while the LDS-direct loads are the kernel's only
+  // vector-memory instructions in the loop: the build refuses a spill
+  // (scratch loads and stores would count too), and so does the launcher.
   const int KT = (k_end - k_begin + BK2 - 1) / BK2;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
@@ -494,7 +497,7 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
 
 template <int LAYOUT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
-  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_bf16<LAYOUT, EPI>>();
+  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_bf16<LAYOUT, EPI>, true>();
   if (e != hipSuccess) return e;
   const int ntc = (a.N + BN2 - 1) / BN2;
   int mtb = 0;

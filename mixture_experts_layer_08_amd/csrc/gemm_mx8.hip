@@ -202,6 +202,9 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
   // refills slot (kt-1) % 4, whose reads every wave finished before this
   // iteration's barrier.  Loads younger than step kt+1 at the wait: step
   // kt+2's four data loads, plus its scale word when kt+2 is even.
+  // The counts assume these LDS-direct loads are the only vector-memory
+  // instructions in the loop: the build refuses a spill (its scratch loads
+  // and stores would count too), and so does the launcher.
   const int KT = Kd / kMxBK;
   issue_step(0);
   issue_step(1);
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
 
 template <int EPI>
 static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
-  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_mx8<EPI>>();
+  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_mx8<EPI>, true>();
   if (e != hipSuccess) return e;
   if (a.Kd <= 0 || a.Kd % kMxBK != 0 || a.N <= 0 || a.N % kMxBlock != 0) return hipErrorInvalidValue;
   const int ntc = (a.N + kMxBN - 1) / kMxBN;

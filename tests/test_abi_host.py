@@ -34,6 +34,16 @@ def test_exports_every_header_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_status_codes_match_the_header():
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "moe.h")).read()
+    enum = dict((n, int(v)) for n, v in re.findall(r"\b(MOE_(?:OK|ERR_[A-Z_]+))\s*=\s*(-?\d+)", src))
+    assert enum == {"MOE_OK": 0, "MOE_ERR_INVALID_ARG": -1, "MOE_ERR_UNSUPPORTED": -2,
+                    "MOE_ERR_WORKSPACE": -3, "MOE_ERR_HIP": -4}
+    for n, v in enum.items():
+        assert getattr(B, n) == v, n
+
+
 def test_status_strings(lib):
     for st in (B.MOE_OK, B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE,
                B.MOE_ERR_HIP):
@@ -298,3 +308,40 @@ def test_mxfp8_calls_reject_bad_arguments_before_launch(lib):
     assert lib.moe_mx_weight_code_bytes(2 ** 20, 2 ** 20, 2 ** 20) == 2 ** 60
     assert lib.moe_mx_operand_scale_bytes(2 ** 62, 2 ** 40) == 0  # overflow
     assert lib.moe_mx_operand_scale_bytes(-1, 128) == 0
+
+
+# ---------------------------------------------------------------- build checks
+
+def test_build_refuses_scratch_in_wait_counted_kernels():
+    """The grouped GEMMs order their LDS ring with hand-counted vmcnt waits;
+    the build's resource check must refuse a spill in them (and only them)."""
+    from mixture_experts_layer_08_amd import build as BLD
+
+    remarks = "\n".join([
+        "gemm.hip:1:1: remark: Function Name: _ZN3moe19k_grouped_gemm_bf16ILi0ELi1EEEvv [-Rpass]",
+        "gemm.hip:1:1: remark:     VGPRs: 256 [-Rpass]",
+        "gemm.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass]",
+        "gemm.hip:1:1: remark:     VGPRs Spill: 4 [-Rpass]",
+        "route.hip:1:1: remark: Function Name: _ZN3moe12k_route_bf16ILi1EEEvv [-Rpass]",
+        "route.hip:1:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass]",
+    ])
+    usage = BLD.resource_usage(remarks)
+    assert usage["_ZN3moe19k_grouped_gemm_bf16ILi0ELi1EEEvv"]["VGPRs Spill"] == "4"
+    with pytest.raises(RuntimeError, match="must not use scratch"):
+        BLD.check_resources(usage)
+    del usage["_ZN3moe19k_grouped_gemm_bf16ILi0ELi1EEEvv"]
+    BLD.check_resources(usage)  # scratch elsewhere is allowed
+
+
+def test_built_grouped_gemms_use_no_scratch():
+    """The resource summary of the last build: every grouped-GEMM
+    instantiation without scratch or spills."""
+    from mixture_experts_layer_08_amd import build as BLD
+
+    path = os.path.join(BLD.BUILD, "resource_usage.txt")
+    if not os.path.exists(path):
+        pytest.skip("no build summary (run the build first)")
+    lines = [l for l in open(path) if any(k in l for k in BLD.NO_SCRATCH_KERNELS)]
+    assert lines, "no grouped-GEMM kernels in the build summary"
+    for l in lines:
+        assert "ScratchSize [bytes/lane]=0" in l and "VGPRs Spill=0" in l, l

@@ -11,25 +11,23 @@ Protocol:
   4. the FP8 results of the GEMMs (h, out, and the shared expert's) are
      quantised by both sides from float32 values that differ by accumulation
      order (and by the MFMA's internal precision), so a value near a rounding
-     boundary may land on the neighbouring code.  h differs only by such
-     decisions: at least 99% of its dequantised values equal and every one
-     within one E4M3 step (plus 2^X of its block).  Stricter, on sampled
-     rows: every GPU h value must be the round-to-nearest, at the GPU's own
-     block scale, of some value within delta of the oracle's unquantised
-     GELU output, where delta bounds the GPU's accumulation and GELU error
-     (check_h_rounding), and every GPU block scale the shared exponent of a
-     block maximum within delta of the oracle's.  A neighbouring code is
-     therefore accepted only where the oracle's value lies within delta of
-     the midpoint between the two codes.  An output row then sums
-     those h values: each neighbouring-code h_j moves output n by up to an
-     eighth of |h_j W2[j, n]|, and with h_exp = 14336 a row carries about a
-     dozen of them, so a few percent of outputs land on the neighbouring code
-     too.  Required for out: at least 90% equal (a wrong rounding rule would
-     move about half) and every value within one step plus 16 * 2^X (a
-     sixteenth to a thirty-second of its block's maximum);
-  5. y (bf16): every element within the sum over its kept slots of
-     |w| times that output bound, plus one bf16 rounding; relative Frobenius
-     error <= 1e-2.
+     boundary may land on the neighbouring code.  Each is checked link by
+     link of the chain, every value (tests/mx_checks.py):
+       - h: every GPU code must be the round-to-nearest, at the GPU's own
+         block scale, of some value within delta of the oracle's unquantised
+         GELU output, and every block scale the shared exponent of a block
+         maximum within delta of the oracle's; delta bounds the GPU's
+         accumulation and GELU error (check_h_rounding).  A neighbouring code
+         is therefore accepted only where the oracle's value lies within
+         delta of the midpoint between the two codes.  On all rows with an
+         upper bound of the per-step maxima from two matmuls, and on sampled
+         rows with the exact maxima;
+       - out: the same rule against the float64 product of the GPU's own
+         dequantised h and the dequantised W2 (check_out_rounding), every row;
+       - the shared expert's h and out likewise;
+  5. y (bf16): every element equal to combine's definition on the GPU's own
+     dequantised outputs (fp32 accumulation, one bf16 rounding); and against
+     the oracle's whole FP8 layer, relative Frobenius error <= 1e-2.
 """
 
 import sys
@@ -43,6 +41,8 @@ from mixture_experts_layer_08_amd import layer
 from mixture_experts_layer_08_amd.inputs import WORKLOADS, Workload, make_inputs, sample_tokens
 from oracle import moe_oracle as O
 from oracle import mxfp8_oracle as M
+from tests.mx_checks import (accum_bounds, accum_bounds_fast, check_combine_definition,
+                             check_h_rounding, check_mx_close, check_out_rounding)
 from tests.test_gpu_parity import check_routing
 
 pytestmark = pytest.mark.gpu
@@ -108,97 +108,6 @@ def oracle_mx(w: Workload, p: dict, buf):
                            np32(p["ws1"]), np32(p["ws2"]), K=w.K, cf=w.cf, logits=l)
 
 
-def step_of(codes, scales_rows):
-    """E4M3 spacing at each element times its block's 2^X (the step to the
-    next larger magnitude; 32 * 2^X at 448)."""
-    c = codes.astype(np.int64) & 0x7F
-    pos = M.e4m3_value(np.arange(0x7F))
-    nxt = np.where(c < 0x7E, pos[np.minimum(c + 1, 0x7E)] - pos[np.minimum(c, 0x7E)], 32.0)
-    X = np.repeat(scales_rows.astype(np.int64) - 127, 32, axis=1)
-    return nxt * np.exp2(X), np.exp2(X)
-
-
-def check_mx_close(name, gc, gs, rc, rs, min_exact=0.99, units=1.0):
-    """Dequantised GPU vs oracle MXFP8 tensors (codes [R][C], row-layout
-    scales): each value within one step plus ``units`` * 2^X of its block."""
-    a = M.mx_dequantize(gc, gs, axis=1)
-    b = M.mx_dequantize(rc, rs, axis=1)
-    sa, ua = step_of(gc, gs)
-    sb, ub = step_of(rc, rs)
-    tol = np.maximum(sa, sb) + units * np.maximum(ua, ub)
-    d = np.abs(a - b)
-    exact = float(np.mean(d == 0)) if d.size else 1.0
-    worst = float(np.max(d / tol)) if d.size else 0.0
-    say(f"  {name}: {d.size} values, {exact:.5%} equal, scales equal {np.mean(gs == rs):.5%}, "
-        f"worst |diff| / tol {worst:.3f}")
-    assert exact >= min_exact, f"{name}: only {exact:.4%} equal"
-    assert worst <= 1.0, f"{name}: a value off by more than the bound"
-    return tol
-
-
-# A 64-value step of v_mfma_scale_f32_32x32x64_f8f6f4 is exact to within 2^-11
-# of its largest product (measured on adversarial codes; the kernel relies on
-# the same property, documented with it).
-MFMA_STEP_REL = 2.0 ** -11
-GELU_SLOPE_MAX = 1.13  # max |d GELU_tanh / du| is 1.1289 (at u = 1.48)
-
-
-def accum_bounds(xd, wd):
-    """For every (row, column) of xd @ wd: the sum over 64-value K-steps of the
-    step's largest |x_k w_kn|, and the sum of all |x_k w_kn| (float64)."""
-    R, Kd = xd.shape
-    n = wd.shape[1]
-    tmax = np.zeros((R, n))
-    tsum = np.abs(xd) @ np.abs(wd)
-    chunk = max(1, (8 << 20) // max(64 * n, 1))
-    for r0 in range(0, R, chunk):
-        xa = np.abs(xd[r0:r0 + chunk])
-        for k0 in range(0, Kd, 64):
-            prod = xa[:, k0:k0 + 64, None] * np.abs(wd[None, k0:k0 + 64, :])
-            tmax[r0:r0 + chunk] += prod.max(axis=1)
-    return tmax, tsum
-
-
-def check_h_rounding(name, gc, gs, v, tmax, tsum, Kd):
-    """GPU GELU outputs in MXFP8 (codes gc [R][C], row-layout scales gs)
-    against the oracle's unquantised values v [R][C] (float64).
-
-    The GPU quantises its own float32 value v', with |v' - v| <= delta:
-      delta = GELU_SLOPE_MAX * 2 (MFMA_STEP_REL * tmax + (Kd / 64) 2^-24 tsum)
-              + 2^-18 tsum
-    (the scaled MFMA's per-step error, the fp32 accumulation over Kd / 64
-    steps, twice over for margin; then GELU's slope and its float32
-    evaluation).  Round to nearest at the GPU's scale 2^X then puts every
-    value within half a code step of clamp(v', +-448 2^X), so
-      |deq - clamp(v)| <= step / 2 + delta,
-    and the block scale must be the shared exponent of some block maximum
-    within max(delta) of the oracle's."""
-    delta = GELU_SLOPE_MAX * 2.0 * (MFMA_STEP_REL * tmax + (Kd / 64) * 2.0 ** -24 * tsum) \
-        + 2.0 ** -18 * tsum
-    deq = M.mx_dequantize(gc, gs, axis=1)
-    X = np.repeat(gs.astype(np.int64) - 127, 32, axis=1)
-    lim = 448.0 * np.exp2(X)
-    vc = np.clip(v, -lim, lim)
-    step, _ = step_of(gc, gs)
-    ratio = np.abs(deq - vc) / (0.5 * step + delta)
-    R, C = v.shape
-    amax = np.abs(v).reshape(R, C // 32, 32).max(axis=2)
-    dmax = delta.reshape(R, C // 32, 32).max(axis=2)
-    lo = M.shared_exponent(np.maximum(amax - dmax, 0.0)) + 127
-    hi = M.shared_exponent(amax + dmax) + 127
-    ref_codes, _ = M.mx_quantize(v, axis=1)
-    diff = gc != ref_codes
-    mism = int(np.sum(diff))
-    # how much of delta a differing code uses: (|deq - v| - step/2) / delta
-    used = float(np.max((np.abs(deq - vc) - 0.5 * step)[diff] / delta[diff])) if mism else 0.0
-    say(f"  {name}: {v.size} values, {mism} codes differ from the oracle's (using at most "
-        f"{used:.2f} of delta); worst |deq - v| / (step/2 + delta) {float(ratio.max()):.3f}; scales in range "
-        f"{float(np.mean((gs >= lo) & (gs <= hi))):.5%}; median delta / step "
-        f"{float(np.median(delta / step)):.2e}")
-    assert float(ratio.max()) <= 1.0, f"{name}: a value is not a rounding of the oracle's"
-    assert np.all((gs >= lo) & (gs <= hi)), f"{name}: a block scale off the oracle's maximum"
-
-
 def check_h_sample(w, p, buf, ref, r, nmax, n_rows=256, seed=17):
     """check_h_rounding on up to n_rows packed rows (seeded, across segments)
     and, with a shared expert, on up to n_rows tokens of its h."""
@@ -227,12 +136,31 @@ def check_h_sample(w, p, buf, ref, r, nmax, n_rows=256, seed=17):
                          op_rows(buf.hsh_s, w.T, w.hs)[ts], ref["sh_h"][ts], tmax, tsum, w.H)
 
 
+def check_out_all(name, gc, gs, hd, w2d, off, E):
+    """check_out_rounding on every packed row: the reference of segment e is
+    the float64 product of the GPU's own dequantised h rows hd and expert
+    e's dequantised W2 (w2d [E][h][H]); step maxima bounded by
+    accum_bounds_fast."""
+    R, n = gc.shape
+    v = np.zeros((R, n))
+    tmax = np.zeros((R, n))
+    tsum = np.zeros((R, n))
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if b > a:
+            v[a:b] = hd[a:b] @ w2d[e]
+            tmax[a:b], tsum[a:b] = accum_bounds_fast(hd[a:b], w2d[e])
+    check_out_rounding(name, gc, gs, v, tmax, tsum, hd.shape[1])
+    return v
+
+
 def check_forward(w: Workload, p: dict, buf, mw, ref=None):
     r = check_routing(w, buf)
     ref = ref if ref is not None else oracle_mx(w, p, buf)
     N = int(buf.offsets[-1].item())
     nmax = buf.xp_q.shape[0]
     tok = r["token_of"]
+    off = r["offsets"]
     # byte work: bit-exact
     assert np.array_equal(u8(buf.xp_q[:N]), ref["x_codes"][tok]), "dispatched codes differ"
     assert np.array_equal(op_rows(buf.xp_s, nmax, w.H)[:N], ref["x_scales"][tok]), \
@@ -240,34 +168,51 @@ def check_forward(w: Workload, p: dict, buf, mw, ref=None):
     if w.hs:
         assert np.array_equal(u8(buf.x_q), ref["x_codes"]), "shared-expert x codes differ"
         assert np.array_equal(op_rows(buf.x_s, w.T, w.H), ref["x_scales"])
-    # GEMM results: neighbouring codes allowed at rounding boundaries
-    check_mx_close("h", u8(buf.h_q[:N]), op_rows(buf.h_s, nmax, w.h)[:N], ref["h_codes"],
-                   ref["h_scales"])
-    tol_out = check_mx_close("out", u8(buf.out_q[:N]), u8(buf.out_s[:N]), ref["o_codes"],
-                             ref["o_scales"], min_exact=0.9, units=16.0)
+    xd = M.mx_dequantize(ref["x_codes"], ref["x_scales"], axis=1)
+    w1d = M.mx_dequantize(ref["w1_codes"], ref["w1_scales"], axis=1)
+    w2d = M.mx_dequantize(ref["w2_codes"], ref["w2_scales"], axis=1)
+    # h against the oracle's unquantised GELU output, every row (bounds of
+    # the step maxima from accum_bounds_fast), then sampled rows with the
+    # exact step maxima; the share of equal codes is reported too
+    h_c, h_s = u8(buf.h_q[:N]), op_rows(buf.h_s, nmax, w.h)[:N]
+    check_mx_close("h", h_c, h_s, ref["h_codes"], ref["h_scales"])
+    if N:
+        tmax = np.zeros((N, w.h))
+        tsum = np.zeros((N, w.h))
+        for e in range(w.E):
+            a, b = int(off[e]), int(off[e + 1])
+            if b > a:
+                tmax[a:b], tsum[a:b] = accum_bounds_fast(xd[tok[a:b]], w1d[e])
+        check_h_rounding("h (all rows)", h_c, h_s, ref["h"], tmax, tsum, w.H)
+        del tmax, tsum
     check_h_sample(w, p, buf, ref, r, nmax)
-    tol_sh = None
+    # out against the float64 product of the GPU's own h and W2, every row
+    o_c, o_s = u8(buf.out_q[:N]), u8(buf.out_s[:N])
+    hd = M.mx_dequantize(h_c, h_s, axis=1)
+    if N:
+        check_out_all("out (all rows)", o_c, o_s, hd, w2d, off, w.E)
+    out_d = M.mx_dequantize(o_c, o_s, axis=1) if N else np.zeros((0, w.H))
+    sh_d = None
     if w.hs:
-        check_mx_close("shared h", u8(buf.hsh_q), op_rows(buf.hsh_s, w.T, w.hs),
-                       ref["sh_h_codes"], ref["sh_h_scales"])
-        tol_sh = check_mx_close("shared out", u8(buf.sh_q), u8(buf.sh_s), ref["sh_codes"],
-                                ref["sh_scales"], min_exact=0.9, units=16.0)
+        sh_hc, sh_hs = u8(buf.hsh_q), op_rows(buf.hsh_s, w.T, w.hs)
+        check_mx_close("shared h", sh_hc, sh_hs, ref["sh_h_codes"], ref["sh_h_scales"])
+        ws1d = M.mx_roundtrip(np32(p["ws1"]), axis=0)
+        ws2d = M.mx_roundtrip(np32(p["ws2"]), axis=0)
+        tmax, tsum = accum_bounds_fast(xd, ws1d)
+        check_h_rounding("shared h (all tokens)", sh_hc, sh_hs, ref["sh_h"], tmax, tsum, w.H)
+        check_out_all("shared out (all tokens)", u8(buf.sh_q), u8(buf.sh_s),
+                      M.mx_dequantize(sh_hc, sh_hs, axis=1), ws2d[None], [0, w.T], 1)
+        sh_d = M.mx_dequantize(u8(buf.sh_q), u8(buf.sh_s), axis=1)
+    # y: combine's definition on the GPU's own outputs (every element), and
+    # the whole layer against the oracle's float64 y
     got = buf.y.cpu().to(torch.float64).numpy()
+    check_combine_definition("y", got, out_d, r["row_of"],
+                             buf.topk_w.cpu().numpy().astype(np.float64), sh_d)
     want = ref["y"]
-    bound = np.zeros_like(want)
-    ro, wt = r["row_of"], r["w"]
-    for k in range(w.K):
-        m = ro[:, k] >= 0
-        bound[m] += np.abs(wt[m, k])[:, None] * tol_out[ro[m, k]]
-    if tol_sh is not None:
-        bound += tol_sh
-    bound += 2.0 ** -8 * np.abs(want) + 1e-30  # bf16 rounding of y
-    worst = float(np.max(np.abs(got - want) / bound))
     err = float(np.abs(got - want).max()) / max(float(np.abs(want).max()), 1e-30)
     fro = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
-    say(f"  y: worst |diff| / bound {worst:.3f}, max rel err {err:.3e}, relative Frobenius "
-        f"error {fro:.3e} (tol 1e-2)")
-    assert worst <= 1.0
+    say(f"  y vs the oracle's FP8 layer: max rel err {err:.3e}, relative Frobenius error "
+        f"{fro:.3e} (tol 1e-2)")
     assert fro <= 1e-2
     return r, ref
 
@@ -385,7 +330,8 @@ def test_mixtral_full_size_sampled():
     configuration.  Routing complete and bit-exact; dispatched codes of a
     token sample bit-exact; weight codes of sampled columns bit-exact; 16
     packed rows of each of two experts against the oracle's FP8 expert FFN
-    (all h columns, four 32-column blocks of out); y of sampled tokens
+    (all h columns; four 32-column blocks of out against the product of the
+    GPU's own h rows and W2); y of sampled tokens
     against combine's definition on the GPU's out rows (a property that holds
     at any size)."""
     w = WORKLOADS["mixtral_bf16"]
@@ -435,15 +381,16 @@ def test_mixtral_full_size_sampled():
         check_h_rounding(f"h rows of expert {e} (strict)",
                          u8(buf.h_q[torch.as_tensor(rows, device="cuda")]),
                          op_rows(buf.h_s, nmax, w.h)[rows], hv, tmax, tsum, w.H)
+        # out columns against the float64 product of the GPU's own h rows
+        # and the dequantised W2 columns (exact step maxima)
+        rt = torch.as_tensor(rows, device="cuda")
+        gh_c, gh_s = u8(buf.h_q[rt]), op_rows(buf.h_s, nmax, w.h)[rows]
+        check_mx_close(f"h rows of expert {e}", gh_c, gh_s, hc, hs)
+        hd = M.mx_dequantize(gh_c, gh_s, axis=1)
         w2d = M.mx_roundtrip(np32(p["w2"][e][:, torch.as_tensor(ocols, device="cuda")]), axis=0)
-        o = M.mx_dequantize(hc, hs, axis=1) @ w2d
-        oc, osc = M.mx_quantize(o, axis=1)
-        check_mx_close(f"h rows of expert {e}", u8(buf.h_q[torch.as_tensor(rows, device="cuda")]),
-                       op_rows(buf.h_s, nmax, w.h)[rows], hc, hs)
-        gout = u8(buf.out_q[torch.as_tensor(rows, device="cuda")])[:, ocols]
-        gsc = u8(buf.out_s[torch.as_tensor(rows, device="cuda")])[:, blocks]
-        check_mx_close(f"out rows of expert {e}", gout, gsc, oc, osc, min_exact=0.9,
-                       units=16.0)
+        tmax, tsum = accum_bounds(hd, w2d)
+        check_out_rounding(f"out rows of expert {e} (strict)", u8(buf.out_q[rt])[:, ocols],
+                           u8(buf.out_s[rt])[:, blocks], hd @ w2d, tmax, tsum, w.h)
     # y against combine's definition on the GPU's own FP8 outputs
     y = buf.y.cpu().to(torch.float64).numpy()
     for t in toks[:64]:

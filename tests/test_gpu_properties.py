@@ -7,8 +7,10 @@ an optional shared expert and a logits mode:
     passed with MOE_FLAG_LOGITS_IN (the tie rule and the drop order under
     pressure);
   * "router": the GPU's own router GEMM on seeded inputs.
-Routing is then bit-exact against the oracle on the GPU's logits, and y is
-within the tolerance of its dtype, as in the fixed-shape parity tests.
+Routing is then bit-exact against the oracle on the GPU's logits, the GPU's
+own logits (router mode) within the fp32-sum bound of the oracle's float64
+router GEMM, and y within the tolerance of its dtype and its per-element
+bound, as in the fixed-shape parity tests.
 Derandomised: every run draws the same examples.
 """
 
@@ -21,7 +23,7 @@ from hypothesis import strategies as st
 from mixture_experts_layer_08_amd import binding as B
 from mixture_experts_layer_08_amd import layer
 from mixture_experts_layer_08_amd.inputs import Workload, make_inputs
-from tests.test_gpu_parity import check_routing, check_y
+from tests.test_gpu_parity import check_logits, check_routing, check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -64,4 +66,6 @@ def test_random_shapes(c):
     layer.forward(buf, p)
     torch.cuda.synchronize()
     routing = check_routing(w, buf)
+    if not given_logits:
+        check_logits(w, p, buf)
     check_y(w, p, buf, routing)
