@@ -32,7 +32,7 @@ int64_t capacity_of(const moe_shape* s) {
 }
 
 struct WsLayout {
-  size_t wT, hist, psum, base, lrank;
+  size_t wT, hist, psum, base, lrank, cnt, seg;
   // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
   // weight gradient's partials, and bf16 copies of d_logits / W_r padded to
   // a multiple of 8 experts for the d_logits * W_r^T GEMM
@@ -59,6 +59,10 @@ WsLayout ws_layout(const moe_shape* s) {
   off += align_up((size_t)s->E * nblk * 4);
   L.lrank = off;
   off += align_up((size_t)s->T * s->K * 4);
+  L.cnt = off;
+  off += align_up((size_t)s->E * 4);
+  L.seg = off;
+  off += align_up((size_t)(2 * s->E + 2) * 4);
   if (s->flags & MOE_FLAG_TRAIN) {
     const size_t elem = s->dtype == MOE_BF16 ? 2 : 4;
     const size_t nch = (size_t)route_bwd_chunks(s->T, s->E);
@@ -291,8 +295,10 @@ moe_status moe_aux_loss(const moe_shape* s, const void* ws, size_t ws_bytes, flo
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   void* w = const_cast<void*>(ws);
-  return hip_status(launch_aux(at<int32_t>(w, L.hist), at<float>(w, L.psum), aux, s->T, s->E,
-                               s->K, n_route_blocks(s), (hipStream_t)stream));
+  return hip_status(launch_aux(at<int32_t>(w, L.hist), at<float>(w, L.psum), aux,
+                               at<int32_t>(w, L.base), at<int32_t>(w, L.cnt),
+                               at<int32_t>(w, L.seg), s->T, s->E, s->K, (int)capacity_of(s),
+                               n_route_blocks(s), (hipStream_t)stream));
 }
 
 moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_ids, void* ws,
@@ -311,9 +317,10 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_id
   a.bf16 = s->dtype == MOE_BF16;
   a.x = x;
   a.topk_ids = topk_ids;
-  a.hist = at<int32_t>(ws, L.hist);
   a.lrank = at<int32_t>(ws, L.lrank);
   a.base = at<int32_t>(ws, L.base);
+  a.cnt = at<int32_t>(ws, L.cnt);
+  a.seg = at<int32_t>(ws, L.seg);
   a.counts = counts;
   a.kept = kept;
   a.offsets = offsets;
@@ -611,9 +618,10 @@ moe_status moe_permute_mxfp8(const moe_shape* s, const void* x, const int32_t* t
   PermuteMx8Args a{};
   a.x = x;
   a.topk_ids = topk_ids;
-  a.hist = at<int32_t>(ws, L.hist);
   a.lrank = at<int32_t>(ws, L.lrank);
   a.base = at<int32_t>(ws, L.base);
+  a.cnt = at<int32_t>(ws, L.cnt);
+  a.seg = at<int32_t>(ws, L.seg);
   a.counts = counts;
   a.kept = kept;
   a.offsets = offsets;

@@ -12,7 +12,12 @@ namespace moe {
 // One wave per token.  y[t] = sum_k w[t,k] out[row_of[t,k]] over kept slots,
 // accumulated in fp32 in slot order (fused multiply-add), then + shared[t],
 // then rounded to the output dtype.  Each expert-output row is read once,
-// each token row written once, in 16-byte vectors.
+// each token row written once, in 16-byte vectors.  Both streams are
+// non-temporal: the expert outputs are read once and y is not read again
+// by this forward.  Measured at T=32768, H=4096, E=8, top-2: 144 -> 131 us,
+// and the next router call, which reads x right after this kernel, 82 ->
+// 65 us, since y no longer leaves dirty lines in the caches for it to evict.
+// (Non-temporal stores alone: 150 us.)
 template <bool BF16, int VPL>
 __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ out,
                                                  const int32_t* __restrict__ row_of,
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ out,
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
           const int c = c0 + lane + 64 * j;
-          if (c < nvec) v[j] = src[c];
+          if (c < nvec) v[j] = __builtin_nontemporal_load(src + c);
         }
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ out,
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[j][q]);
         }
-        y[(size_t)t * nvec + c] = o;
+        __builtin_nontemporal_store(o, y + (size_t)t * nvec + c);
       }
     }
   }
@@ -124,12 +129,108 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
 // of two): thread (e, g) sums blocks g, g+G, g+2G, ... in order (fp64), then a
 // fixed-shape tree over g combines them, and thread 0 adds the per-expert
 // terms in expert order.  Deterministic: every sum has a fixed order.
+//
+// The same workgroup then does the permutation's block scan (integer sums,
+// so exact and deterministic): base[e][b] = sum_{b' < b} hist[e][b'] and
+// cnt[e] = sum_b hist[e][b].  Wave w takes experts w, w + 16, ...; lane l
+// holds 8 consecutive blocks of a 512-block chunk, and the loads of up to 4
+// experts are in flight before any is summed.  Wave 0 then derives the
+// segments: kept[e] = min(cnt[e], C), offsets = exclusive scan of kept (E+1
+// entries), and the number of dropped assignments, into seg = [offsets (E+1)
+// | kept (E) | n_dropped].  Doing this here rather than in kernels of their
+// own saves moe_permute its dependent launches and leaves it one load per
+// index.
 constexpr int kAuxThreads = 1024;
+
+__device__ void block_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+                           int32_t* __restrict__ cnt, int* s_cnt, int E, int nblk) {
+  constexpr int kPer = 8;    // blocks per lane per chunk
+  constexpr int kBatch = 4;  // experts whose loads are in flight together
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int e0 = wave; e0 < E; e0 += nwaves * kBatch) {
+    int carry[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) carry[j] = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
+      int v[kBatch][kPer];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = e0 + j * nwaves;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int b = b0 + lane * kPer + i;
+          v[j][i] = e < E && b < nblk ? hist[(size_t)e * nblk + b] : 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = e0 + j * nwaves;
+        if (e >= E) break;  // wave-uniform
+        int s = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) s += v[j][i];
+        const int incl = wave_inclusive_scan(s);
+        int run = carry[j] + incl - s;
+        int32_t* bo = base + (size_t)e * nblk;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int b = b0 + lane * kPer + i;
+          if (b < nblk) bo[b] = run;
+          run += v[j][i];
+        }
+        carry[j] += __shfl(incl, 63, kWave);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (e0 + j * nwaves < E) {
+          cnt[e0 + j * nwaves] = carry[j];
+          s_cnt[e0 + j * nwaves] = carry[j];
+        }
+    }
+  }
+}
+
+// Wave 0: seg = [offsets (E+1) | kept (E) | n_dropped] from the counts in
+// LDS (E <= 256: lane l holds experts 4l .. 4l+3).
+__device__ void segments(const int* s_cnt, int32_t* __restrict__ seg, int E, int C) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  int kept4[4], run = 0, drop = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    const int c = e < E ? s_cnt[e] : 0;
+    kept4[i] = min(c, C);
+    drop += c - kept4[i];
+    run += kept4[i];
+  }
+  const int incl = wave_inclusive_scan(run);
+  int off = incl - run;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * lane + i;
+    if (e < E) {
+      seg[e] = off;
+      seg[E + 1 + e] = kept4[i];
+    }
+    off += kept4[i];
+  }
+  const int dropped = wave_sum(drop);
+  if (lane == 63) seg[E] = incl;
+  if (lane == 0) seg[2 * E + 1] = dropped;
+}
 __global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__ hist,
                                                      const float* __restrict__ psum,
-                                                     float* __restrict__ aux, int T, int E, int K,
-                                                     int nblk) {
+                                                     float* __restrict__ aux,
+                                                     int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ cnt_out,
+                                                     int32_t* __restrict__ seg, int T, int E,
+                                                     int K, int C, int nblk) {
   __shared__ double s_p[kAuxThreads];
+  __shared__ int s_cnt[256];
   __shared__ long long s_c[kAuxThreads];
   int e_pad = 1;
   while (e_pad < E) e_pad <<= 1;
@@ -160,11 +261,15 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__
       s += ((double)s_c[i * G] / ((double)T * K)) * (s_p[i * G] / (double)T);
     *aux = (float)((double)E * s);
   }
+  block_scan(hist, base, cnt_out, s_cnt, E, nblk);
+  __syncthreads();
+  segments(s_cnt, seg, E, C);
 }
 
-hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int T, int E, int K,
-                      int nblk, hipStream_t st) {
-  k_aux<<<1, kAuxThreads, 0, st>>>(hist, psum, aux, T, E, K, nblk);
+hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int32_t* base,
+                      int32_t* cnt, int32_t* seg, int T, int E, int K, int C, int nblk,
+                      hipStream_t st) {
+  k_aux<<<1, kAuxThreads, 0, st>>>(hist, psum, aux, base, cnt, seg, T, E, K, C, nblk);
   return hipGetLastError();
 }
 

@@ -52,9 +52,10 @@ struct PermuteArgs {
   bool bf16;
   const void* x;
   const int32_t* topk_ids;
-  const int32_t* hist;
   const int32_t* lrank;
-  int32_t* base;       // [E][nblk] scratch
+  const int32_t* base;  // [E][nblk] from moe_aux_loss's block scan
+  const int32_t* cnt;   // [E] per-expert assignment counts, from the same scan
+  const int32_t* seg;   // [2E + 2] offsets, kept, n_dropped, from the same scan
   int32_t* counts;
   int32_t* kept;
   int32_t* offsets;
@@ -73,9 +74,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 struct PermuteMx8Args {
   const void* x;       // bf16 [T][H]
   const int32_t* topk_ids;
-  const int32_t* hist;
   const int32_t* lrank;
-  int32_t* base;
+  const int32_t* base;
+  const int32_t* cnt;
+  const int32_t* seg;
   int32_t* counts;
   int32_t* kept;
   int32_t* offsets;
@@ -178,8 +180,14 @@ hipError_t launch_combine_mx8(const CombineMx8Args& a, hipStream_t st);
 hipError_t launch_quantize_weight_mx8(const void* w, bool bf16_in, int G, int Kd, int N,
                                       uint8_t* q, uint8_t* s, hipStream_t st);
 
-hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int T, int E, int K,
-                      int nblk, hipStream_t st);
+// The aux loss from the router's per-block partials, and in the same
+// workgroup the permutation's block scan: base [E][nblk] = per-expert
+// exclusive prefix over route blocks of the block histograms, cnt [E] = the
+// per-expert totals, seg [2E + 2] = segment offsets (E + 1), kept (E) and
+// the number of dropped assignments at capacity C.
+hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int32_t* base,
+                      int32_t* cnt, int32_t* seg, int T, int E, int K, int C, int nblk,
+                      hipStream_t st);
 
 // ---- backward ----
 struct CombineBwdArgs {

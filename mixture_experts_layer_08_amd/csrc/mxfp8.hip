@@ -76,7 +76,9 @@ hipError_t launch_quantize_weight_mx8(const void* w, bool bf16_in, int G, int Kd
 // (+ deq(shared[t])), accumulated in fp32 in slot order (fused multiply-add;
 // the dequantised values are exact in fp32), rounded to bf16.  A lane takes
 // 16 code bytes (half a block) per vector and its block's scale byte (row
-// layout); each token row is written once as bf16.
+// layout); each token row is written once as bf16.  Code loads and y stores
+// are non-temporal, as in the bf16 combine (T=32768, H=4096, E=8: 119 ->
+// 115 us, and the next router call 81 -> 63 us).
 template <int VPL>
 __global__ __launch_bounds__(256) void k_combine_mx8(const u32x4* __restrict__ out_q,
                                                      const uint8_t* __restrict__ out_s,
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void k_combine_mx8(const u32x4* __restrict__ o
       for (int j = 0; j < VPL; ++j) {
         const int c = c0 + lane + 64 * j;
         if (c < nvec) {
-          v[j] = src[c];
+          v[j] = __builtin_nontemporal_load(src + c);
           sc[j] = ssrc[c >> 1];
         }
       }
@@ -152,8 +154,8 @@ __global__ __launch_bounds__(256) void k_combine_mx8(const u32x4* __restrict__ o
           o0[q] = pack_bf16x2(acc[j][2 * q], acc[j][2 * q + 1]);
           o1[q] = pack_bf16x2(acc[j][8 + 2 * q], acc[j][8 + 2 * q + 1]);
         }
-        y[(size_t)t * 2 * nvec + 2 * c] = o0;
-        y[(size_t)t * 2 * nvec + 2 * c + 1] = o1;
+        __builtin_nontemporal_store(o0, y + (size_t)t * 2 * nvec + 2 * c);
+        __builtin_nontemporal_store(o1, y + (size_t)t * 2 * nvec + 2 * c + 1);
       }
     }
   }

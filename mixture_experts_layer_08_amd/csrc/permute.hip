@@ -11,147 +11,121 @@
 //   base[e][block(t)] + lrank[t,k],
 // where lrank (from the router) is its rank inside its route block and
 // base[e][b] is the exclusive prefix sum over route blocks of the per-block
-// histograms.  Everything is integer arithmetic in a fixed order: the row
-// map is bit-exact and deterministic, with no atomics.
+// histograms (moe_aux_loss's kernel computes it, with the per-expert
+// totals).  Everything is integer arithmetic in a fixed order: the row map
+// is bit-exact and deterministic, with no atomics.
 #include "common.h"
 #include "kernels.h"
 #include "mx.h"
 
 namespace moe {
 
-// One workgroup per expert: base[e][b] = sum_{b' < b} hist[e][b'], counts[e].
-__global__ __launch_bounds__(256) void k_scan_blocks(const int32_t* __restrict__ hist,
-                                                     int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ counts, int nblk) {
-  __shared__ int s_wave[4];
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int32_t* h = hist + (size_t)e * nblk;
-  int32_t* bo = base + (size_t)e * nblk;
-  int carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
-    const int b = b0 + tid;
-    const int v = b < nblk ? h[b] : 0;
-    const int incl = wave_inclusive_scan(v);
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
+// The packed rows of token t's K assignments (-1 when dropped).  t is
+// wave-uniform, so ids, lrank, base and the segment offsets are read with
+// scalar loads, which wait on their own counter (lgkmcnt): the caller issues
+// the token row's vector loads first, and the two latencies overlap.  The
+// checks keep a permutation run on stale or foreign routing results inside
+// the row buffers (from this forward's router and aux-loss calls they always
+// hold: 0 <= e < E, r >= 0, offset + r < the kept total).
+// K is a compile-time constant so that the two rounds of loads (ids and
+// lrank, then base and offsets) are 2K scalar loads each with no branch
+// between them; expert ids are clamped for addressing, then masked.
+template <int K>
+__device__ __forceinline__ void token_rows(int t, const int32_t* __restrict__ ids,
+                                           const int32_t* __restrict__ lrank,
+                                           const int32_t* __restrict__ base,
+                                           const int32_t* __restrict__ seg, int T, int E, int C,
+                                           int nblk, int (&rows)[8]) {
+  const long long max_rows = min((long long)T * K, (long long)E * C);
+  const int blk = t / kRouteBlock;
+  int e[K], lr[K], b[K], o[K];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      before += w < wave ? s_wave[w] : 0;
-      total += s_wave[w];
+  for (int k = 0; k < K; ++k) {
+    e[k] = ids[(size_t)t * K + k];
+    lr[k] = lrank[(size_t)t * K + k];
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int ec = min(max(e[k], 0), E - 1);
+    b[k] = base[(size_t)ec * nblk + blk];
+    o[k] = seg[ec];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    rows[k] = -1;
+    if (k < K) {
+      const int r = b[k] + lr[k];
+      const bool ok = e[k] >= 0 && e[k] < E && r >= 0 && r < C && (long long)o[k] + r < max_rows;
+      rows[k] = ok ? o[k] + r : -1;
     }
-    if (b < nblk) bo[b] = carry + before + incl - v;
-    carry += total;
-    __syncthreads();
   }
-  if (tid == 0) counts[e] = carry;
 }
 
-// Segment offsets from the per-expert counts, computed by every permute wave
-// (E <= 256: lane l holds experts 4l .. 4l+3): kept = min(counts, C),
-// offsets = exclusive scan of kept.  Returns this lane's four offsets and the
-// wave-uniform total; the counts are integers, so every wave gets the same.
-__device__ __forceinline__ void segment_offsets(const int32_t* __restrict__ counts, int E, int C,
-                                                int (&off4)[4], int (&kept4)[4], int& drop4,
-                                                int& total) {
+// Lane k < K writes row_of[t, k] and, for a kept row, token_of; the wave of
+// token 0 also copies the per-expert counts and the segments (offsets, kept,
+// n_dropped) from the workspace to the caller's arrays.
+__device__ __forceinline__ void publish_rows(
+    int t, const int (&rows)[8], const int32_t* __restrict__ cnt, const int32_t* __restrict__ seg,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of, int32_t* __restrict__ token_of,
+    int E, int K) {
   const int lane = threadIdx.x & 63;
-  int run = 0;
-  drop4 = 0;
+  int my = -1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
-    const int c = e < E ? counts[e] : 0;
-    kept4[i] = min(c, C);
-    drop4 += c - kept4[i];
-    off4[i] = run;  // exclusive within the lane
-    run += kept4[i];
-  }
-  const int incl = wave_inclusive_scan(run);
-  const int before = incl - run;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) off4[i] += before;
-  total = __shfl(incl, 63, kWave);
-}
-
-// The row map of token t, computed by its wave: lane k < K returns the packed
-// row of assignment (t, k) (-1 when dropped) and writes row_of / token_of;
-// other lanes return -1.  The wave of token 0 also publishes kept, offsets
-// and n_dropped.  Index loads come first (the counts load independently of
-// ids and lrank, so two dependent round trips precede any row traffic).
-__device__ __forceinline__ int permute_row_map(
-    int t, const int32_t* __restrict__ ids, const int32_t* __restrict__ lrank,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ kept, int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ token_of, int E, int K, int C, int nblk) {
-  const int lane = threadIdx.x & 63;
-  int e = 0, lr = 0;
+  for (int k = 0; k < 8; ++k) my = lane == k ? rows[k] : my;
   if (lane < K) {
-    e = ids[(size_t)t * K + lane];
-    lr = lrank[(size_t)t * K + lane];
+    row_of[(size_t)t * K + lane] = my;
+    if (my >= 0) token_of[my] = t;
   }
-  int off4[4], kept4[4], drop4, total;
-  segment_offsets(counts, E, C, off4, kept4, drop4, total);
   if (t == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ee = 4 * lane + i;
-      if (ee < E) {
-        kept[ee] = kept4[i];
-        offsets[ee] = off4[i];
-      }
+    for (int e = lane; e < E; e += kWave) {
+      counts[e] = cnt[e];
+      offsets[e] = seg[e];
+      kept[e] = seg[E + 1 + e];
     }
-    const int dropped = wave_sum(drop4);
     if (lane == 0) {
-      offsets[E] = total;
-      *n_dropped = dropped;
+      offsets[E] = seg[E];
+      *n_dropped = seg[2 * E + 1];
     }
   }
-  int row = -1;
-  // offsets[e] lives in lane e/4, slot e%4 (all lanes take part in the shuffles)
-  const int o0 = __shfl(off4[0], e >> 2, kWave), o1 = __shfl(off4[1], e >> 2, kWave);
-  const int o2 = __shfl(off4[2], e >> 2, kWave), o3 = __shfl(off4[3], e >> 2, kWave);
-  const int oe = (e & 3) == 0 ? o0 : (e & 3) == 1 ? o1 : (e & 3) == 2 ? o2 : o3;
-  if (lane < K) {
-    const int r = base[(size_t)e * nblk + t / kRouteBlock] + lr;
-    row = r < C ? oe + r : -1;
-    row_of[(size_t)t * K + lane] = row;
-    if (row >= 0) token_of[row] = t;
-  }
-  return row;
 }
 
-// One wave per token: its row map entries, then the copy of its row to each
-// kept destination.  The row is read from HBM once (16-byte vectors, VPL per
-// lane per chunk, all loads of a chunk issued before its stores; vmcnt waits
-// are in issue order, so the row loads come after the index loads).
-template <int VPL>
+// One wave per token: the copy of its row to each kept destination, and its
+// row map entries.  The row is read from HBM once, in 16-byte vectors, VPL
+// per lane per chunk, with non-temporal loads (the dispatch is the last
+// reader of x); the first chunk's loads are issued before the index loads
+// (token_rows), so the row's latency and the indices' overlap.  Measured at
+// T=32768, H=4096, E=8, top-2 (stage times): 154 us with the block scan as a
+// launch of its own and vector index loads, 133 us with the scan in the
+// aux-loss kernel and scalar index loads, 124 us with the non-temporal row
+// loads.  Non-temporal stores of xp were no faster (the grouped GEMM reads
+// xp next).
+template <int VPL, int K>
 __global__ __launch_bounds__(256) void k_permute(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
-    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int E, int K, int C,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ seg,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ token_of, u32x4* __restrict__ xp, int T, int nvec, int E, int C,
     int nblk) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;  // wave-uniform; the kernel has no barrier (token 0 always runs)
   const int lane = threadIdx.x & 63;
-  const int row = permute_row_map(t, ids, lrank, base, counts, kept, offsets, n_dropped, row_of,
-                                  token_of, E, K, C, nblk);
   const u32x4* src = x + (size_t)t * nvec;
   u32x4 v[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nvec) v[j] = __builtin_nontemporal_load(src + c);
+  }
   int rows[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) rows[k] = __shfl(row, k, kWave);
-  for (int c0 = 0; c0 < nvec; c0 += 64 * VPL) {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int c = c0 + lane + 64 * j;
-      if (c < nvec) v[j] = src[c];
-    }
+  token_rows<K>(t, ids, lrank, base, seg, T, E, C, nblk, rows);
+  publish_rows(t, rows, cnt, seg, counts, kept, offsets, n_dropped, row_of, token_of, E, K);
+  for (int c0 = 0;;) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (k < K && rows[k] >= 0) {
+      if (rows[k] >= 0) {
         u32x4* dst = xp + (size_t)rows[k] * nvec;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
@@ -159,6 +133,13 @@ __global__ __launch_bounds__(256) void k_permute(
           if (c < nvec) dst[c] = v[j];
         }
       }
+    }
+    c0 += 64 * VPL;
+    if (c0 >= nvec) break;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int c = c0 + lane + 64 * j;
+      if (c < nvec) v[j] = __builtin_nontemporal_load(src + c);
     }
   }
 }
@@ -170,31 +151,39 @@ __global__ __launch_bounds__(256) void k_permute(
 // lane of every 16, one 4-byte word of four block scales (operand layout,
 // leading dimension xp_ld).  With x_q set the token's own quantised row is
 // also written (row t, leading dimension T), for the shared expert.
-template <int VPL>
+template <int VPL, int K>
 __global__ __launch_bounds__(256) void k_permute_mx8(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ lrank, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ seg,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_dropped, int32_t* __restrict__ row_of,
     int32_t* __restrict__ token_of, u32x2* __restrict__ xp_q, uint8_t* __restrict__ xp_s,
     int xp_ld, u32x2* __restrict__ x_q, uint8_t* __restrict__ x_s, int T, int nvec, int E,
-    int K, int C, int nblk) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int C, int nblk) {
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;  // wave-uniform; no barrier in this kernel
   const int lane = threadIdx.x & 63;
-  const int row = permute_row_map(t, ids, lrank, base, counts, kept, offsets, n_dropped, row_of,
-                                  token_of, E, K, C, nblk);
   const u32x4* src = x + (size_t)t * nvec;
-  int rows[9];
+  // the first chunk of the row before the index loads, as in k_permute
+  u32x4 v[VPL];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) rows[k] = k < K ? __shfl(row, k, kWave) : -1;
+  for (int j = 0; j < VPL; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = c < nvec ? src[c] : u32x4{0u, 0u, 0u, 0u};
+  }
+  int rows[9];
+  token_rows<K>(t, ids, lrank, base, seg, T, E, C, nblk, (int(&)[8])rows);
+  publish_rows(t, (int(&)[8])rows, cnt, seg, counts, kept, offsets, n_dropped, row_of, token_of,
+               E, K);
   rows[8] = x_q ? t : -1;  // the shared expert's copy
   for (int c0 = 0; c0 < nvec; c0 += 64 * VPL) {
-    u32x4 v[VPL];
+    if (c0 > 0) {
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int c = c0 + lane + 64 * j;
-      v[j] = c < nvec ? src[c] : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < VPL; ++j) {
+        const int c = c0 + lane + 64 * j;
+        v[j] = c < nvec ? src[c] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     u32x2 q[VPL];
     uint32_t sw[VPL];
@@ -240,28 +229,47 @@ __global__ __launch_bounds__(256) void k_permute_mx8(
   }
 }
 
+template <int K>
+static void launch_permute_k(const PermuteArgs& a, int nvec, int nblk, hipStream_t st) {
+  k_permute<8, K><<<(a.T + 3) / 4, 256, 0, st>>>(
+      (const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.cnt, a.seg, a.counts, a.kept, a.offsets,
+      a.n_dropped, a.row_of, a.token_of, (u32x4*)a.xp, a.T, nvec, a.E, a.C, nblk);
+}
+
+template <int K>
+static void launch_permute_mx8_k(const PermuteMx8Args& a, int nvec, int nblk, hipStream_t st) {
+  k_permute_mx8<4, K><<<(a.T + 3) / 4, 256, 0, st>>>(
+      (const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.cnt, a.seg, a.counts, a.kept, a.offsets,
+      a.n_dropped, a.row_of, a.token_of, (u32x2*)a.xp_q, a.xp_s, a.xp_ld, (u32x2*)a.x_q, a.x_s,
+      a.T, nvec, a.E, a.C, nblk);
+}
+
+#define MOE_PERMUTE_BY_K(LAUNCH, ...)          \
+  switch (a.K) {                              \
+    case 1: LAUNCH<1>(a, __VA_ARGS__); break; \
+    case 2: LAUNCH<2>(a, __VA_ARGS__); break; \
+    case 3: LAUNCH<3>(a, __VA_ARGS__); break; \
+    case 4: LAUNCH<4>(a, __VA_ARGS__); break; \
+    case 5: LAUNCH<5>(a, __VA_ARGS__); break; \
+    case 6: LAUNCH<6>(a, __VA_ARGS__); break; \
+    case 7: LAUNCH<7>(a, __VA_ARGS__); break; \
+    case 8: LAUNCH<8>(a, __VA_ARGS__); break; \
+    default: return hipErrorInvalidValue;     \
+  }
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int nblk = (a.T + kRouteBlock - 1) / kRouteBlock;
-  k_scan_blocks<<<a.E, 256, 0, st>>>(a.hist, a.base, a.counts, nblk);
-  const int elem = a.bf16 ? 2 : 4;
-  const int nvec = a.H * elem / 16;
-  const int grid = (a.T + 3) / 4;
-  k_permute<8><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base, a.counts,
-                                     a.kept, a.offsets, a.n_dropped, a.row_of, a.token_of,
-                                     (u32x4*)a.xp, a.T, nvec, a.E, a.K, a.C, nblk);
+  const int nvec = a.H * (a.bf16 ? 2 : 4) / 16;
+  MOE_PERMUTE_BY_K(launch_permute_k, nvec, nblk, st)
   return hipGetLastError();
 }
 
 hipError_t launch_permute_mx8(const PermuteMx8Args& a, hipStream_t st) {
   const int nblk = (a.T + kRouteBlock - 1) / kRouteBlock;
-  k_scan_blocks<<<a.E, 256, 0, st>>>(a.hist, a.base, a.counts, nblk);
   const int nvec = a.H / 8;  // 16-byte bf16 chunks per row
-  const int grid = (a.T + 3) / 4;
-  k_permute_mx8<4><<<grid, 256, 0, st>>>((const u32x4*)a.x, a.topk_ids, a.lrank, a.base,
-                                         a.counts, a.kept, a.offsets, a.n_dropped, a.row_of,
-                                         a.token_of, (u32x2*)a.xp_q, a.xp_s, a.xp_ld,
-                                         (u32x2*)a.x_q, a.x_s, a.T, nvec, a.E, a.K, a.C, nblk);
+  MOE_PERMUTE_BY_K(launch_permute_mx8_k, nvec, nblk, st)
   return hipGetLastError();
 }
+#undef MOE_PERMUTE_BY_K
 
 }  // namespace moe

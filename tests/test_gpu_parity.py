@@ -330,3 +330,28 @@ def test_combine_of_permuted_rows_is_identity():
     B.moe_combine(buf.shape, buf.xp, buf.row_of, buf.topk_w, None, y)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), p["x"].view(torch.int16))
+
+
+def test_workspace_garbage_and_reuse():
+    """The router's last workgroup computes the permutation's block scan, found
+    through a ticket word in the workspace that no call clears: a workspace
+    full of garbage (all-ones bytes, then random bytes) and one workspace
+    reused over several forwards of different routings must all give the
+    oracle's row map."""
+    w = Workload("ws_reuse", T=1500, H=64, E=6, K=2, h=64, cf=1.1, bias="normal")
+    buf = layer.MoeBuffers.allocate(w)
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    for i, fill in enumerate(["ones", "random", None, None]):
+        say(f"[ws reuse] forward {i}, workspace {fill or 'as left by the previous call'}")
+        if fill == "ones":
+            buf.ws.fill_(0xFF)
+        elif fill == "random":
+            buf.ws.copy_(torch.randint(0, 256, buf.ws.shape, generator=gen, device="cuda",
+                                       dtype=torch.int32).to(torch.uint8))
+        p = make_inputs(w, seed=40 + i, device="cuda")
+        layer.forward(buf, p)
+        torch.cuda.synchronize()
+        r = check_routing(w, buf)
+        check_permutation_identity(buf, p)
+        if i == 3:
+            check_y(w, p, buf, r)
