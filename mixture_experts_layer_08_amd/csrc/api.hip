@@ -32,7 +32,7 @@ int64_t capacity_of(const moe_shape* s) {
 }
 
 struct WsLayout {
-  size_t wT, hist, psum, base, lrank, cnt, seg;
+  size_t hist, psum, base, lrank, cnt, seg;
   // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
   // weight gradient's partials, and bf16 copies of d_logits / W_r padded to
   // a multiple of 8 experts for the d_logits * W_r^T GEMM
@@ -49,8 +49,6 @@ WsLayout ws_layout(const moe_shape* s) {
   WsLayout L{};
   const size_t nblk = (size_t)n_route_blocks(s);
   size_t off = 0;
-  L.wT = off;
-  if (s->dtype == MOE_BF16) off += align_up((size_t)route_col_tiles(s->E) * 16 * s->H * 2);
   L.hist = off;
   off += align_up((size_t)s->E * nblk * 4);
   L.psum = off;
@@ -259,7 +257,6 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_router,
   a.x = x;
   a.w_r = w_router;
   a.bias = b_router;
-  a.wT = at<void>(ws, L.wT);
   a.logits = logits;
   a.topk_ids = topk_ids;
   a.topk_w = topk_w;

@@ -123,105 +123,46 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// aux = E * sum_e (count_e / (T K)) (P_e) with P_e = (1/T) sum_t p[t,e].
-// One workgroup of kAuxThreads threads.  Expert e's per-block partials are
-// split over G = kAuxThreads / E_pad threads (E_pad = E rounded up to a power
-// of two): thread (e, g) sums blocks g, g+G, g+2G, ... in order (fp64), then a
-// fixed-shape tree over g combines them, and thread 0 adds the per-expert
-// terms in expert order.  Deterministic: every sum has a fixed order.
-//
-// The same workgroup then does the permutation's block scan (integer sums,
-// so exact and deterministic): base[e][b] = sum_{b' < b} hist[e][b'] and
-// cnt[e] = sum_b hist[e][b].  Wave w takes experts w, w + 16, ...; lane l
-// holds 8 consecutive blocks of a 512-block chunk, and the loads of up to 4
-// experts are in flight before any is summed.  Wave 0 then derives the
-// segments: kept[e] = min(cnt[e], C), offsets = exclusive scan of kept (E+1
-// entries), and the number of dropped assignments, into seg = [offsets (E+1)
-// | kept (E) | n_dropped].  Doing this here rather than in kernels of their
-// own saves moe_permute its dependent launches and leaves it one load per
-// index.
+// aux = E * sum_e (count_e / (T K)) (P_e) with P_e = (1/T) sum_t p[t,e],
+// and the permutation's block scan, in one workgroup of kAuxThreads threads
+// that reads each per-block partial once.  Wave w takes experts w, w + 16,
+// ..., two at a time with all their loads in flight together; per expert,
+// in chunks of 512 route blocks, lane l holds blocks b0 + 64 i + l (i < 8),
+// so every load and store is one coalesced 256-byte row:
+//   - counts (integers: exact, any order): base[e][b] = sum_{b' < b}
+//     hist[e][b'] by one wave scan (DPP) per 64 blocks, cnt[e] = the total;
+//   - P (fp64, a fixed order): each lane sums its 8 blocks in block order,
+//     a fixed butterfly over the 64 lanes sums the lanes, chunks add in
+//     chunk order.
+// Thread 0 then adds the per-expert terms in expert order, and wave 0
+// derives the segments: kept[e] = min(cnt[e], C), offsets = exclusive scan
+// of kept (E+1 entries), and the number of dropped assignments, into seg =
+// [offsets (E+1) | kept (E) | n_dropped].  Everything has a fixed order, so
+// the results are deterministic.  Doing the scan and the segments here saves
+// moe_permute dependent launches and leaves it one load per index.
 constexpr int kAuxThreads = 1024;
 
-__device__ void block_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base,
-                           int32_t* __restrict__ cnt, int* s_cnt, int E, int nblk) {
-  constexpr int kPer = 8;    // blocks per lane per chunk
-  constexpr int kBatch = 4;  // experts whose loads are in flight together
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  for (int e0 = wave; e0 < E; e0 += nwaves * kBatch) {
-    int carry[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) carry[j] = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
-      int v[kBatch][kPer];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = e0 + j * nwaves;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int b = b0 + lane * kPer + i;
-          v[j][i] = e < E && b < nblk ? hist[(size_t)e * nblk + b] : 0;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = e0 + j * nwaves;
-        if (e >= E) break;  // wave-uniform
-        int s = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) s += v[j][i];
-        const int incl = wave_inclusive_scan(s);
-        int run = carry[j] + incl - s;
-        int32_t* bo = base + (size_t)e * nblk;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int b = b0 + lane * kPer + i;
-          if (b < nblk) bo[b] = run;
-          run += v[j][i];
-        }
-        carry[j] += __shfl(incl, 63, kWave);
-      }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        if (e0 + j * nwaves < E) {
-          cnt[e0 + j * nwaves] = carry[j];
-          s_cnt[e0 + j * nwaves] = carry[j];
-        }
-    }
-  }
+// Inclusive prefix sum over the 64 lanes with DPP moves (gfx9): four
+// row_shr steps scan each row of 16 lanes (lanes shifted in from outside the
+// row read 0), then row_bcast:15 adds row 0's total to row 1 and row 2's to
+// row 3, and row_bcast:31 adds the total of rows 0-1 to rows 2 and 3.  No
+// LDS round trips, unlike a shuffle-based scan.
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
 }
 
-// Wave 0: seg = [offsets (E+1) | kept (E) | n_dropped] from the counts in
-// LDS (E <= 256: lane l holds experts 4l .. 4l+3).
-__device__ void segments(const int* s_cnt, int32_t* __restrict__ seg, int E, int C) {
-  if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  int kept4[4], run = 0, drop = 0;
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
-    const int c = e < E ? s_cnt[e] : 0;
-    kept4[i] = min(c, C);
-    drop += c - kept4[i];
-    run += kept4[i];
-  }
-  const int incl = wave_inclusive_scan(run);
-  int off = incl - run;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = 4 * lane + i;
-    if (e < E) {
-      seg[e] = off;
-      seg[E + 1 + e] = kept4[i];
-    }
-    off += kept4[i];
-  }
-  const int dropped = wave_sum(drop);
-  if (lane == 63) seg[E] = incl;
-  if (lane == 0) seg[2 * E + 1] = dropped;
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
 }
+
 __global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__ hist,
                                                      const float* __restrict__ psum,
                                                      float* __restrict__ aux,
@@ -229,41 +170,99 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__
                                                      int32_t* __restrict__ cnt_out,
                                                      int32_t* __restrict__ seg, int T, int E,
                                                      int K, int C, int nblk) {
-  __shared__ double s_p[kAuxThreads];
+  __shared__ double s_p[256];
   __shared__ int s_cnt[256];
-  __shared__ long long s_c[kAuxThreads];
-  int e_pad = 1;
-  while (e_pad < E) e_pad <<= 1;
-  const int G = kAuxThreads / e_pad;
-  const int tid = threadIdx.x;
-  const int e = tid / G, g = tid % G;
-  double P = 0.0;
-  long long cnt = 0;
-  if (e < E) {
-    for (int b = g; b < nblk; b += G) {
-      cnt += hist[(size_t)e * nblk + b];
-      P += (double)psum[(size_t)e * nblk + b];
+  constexpr int kPer = 8;    // blocks per lane per chunk
+  constexpr int kBatch = 2;  // experts whose loads are in flight together
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = kAuxThreads / kWave;
+  for (int e0 = wave; e0 < E; e0 += nwaves * kBatch) {
+    int carry[kBatch];
+    double P[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      carry[j] = 0;
+      P[j] = 0.0;
+    }
+    for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
+      int v[kBatch][kPer];
+      float pv[kBatch][kPer];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = e0 + j * nwaves;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int b = b0 + 64 * i + lane;
+          const bool ok = e < E && b < nblk;
+          v[j][i] = ok ? hist[(size_t)e * nblk + b] : 0;
+          pv[j][i] = ok ? psum[(size_t)e * nblk + b] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = e0 + j * nwaves;
+        if (e >= E) break;  // wave-uniform
+        double ps = 0.0;
+        int32_t* bo = base + (size_t)e * nblk;
+        // the 8 wave scans are independent (their shuffles overlap); the
+        // carries from row to row are added afterwards
+        int incl[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) incl[i] = wave_scan_dpp(v[j][i]);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          ps += (double)pv[j][i];
+          const int b = b0 + 64 * i + lane;
+          if (b < nblk) bo[b] = carry[j] + incl[i] - v[j][i];
+          carry[j] += __builtin_amdgcn_readlane(incl[i], 63);
+        }
+        P[j] += wave_sum_f64(ps);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int e = e0 + j * nwaves;
+        if (e < E) {
+          cnt_out[e] = carry[j];
+          s_cnt[e] = carry[j];
+          s_p[e] = P[j];
+        }
+      }
     }
   }
-  s_p[tid] = P;
-  s_c[tid] = cnt;
   __syncthreads();
-  for (int w = G >> 1; w > 0; w >>= 1) {
-    if (g < w) {
-      s_p[tid] += s_p[tid + w];
-      s_c[tid] += s_c[tid + w];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     double s = 0.0;
-    for (int i = 0; i < E; ++i)
-      s += ((double)s_c[i * G] / ((double)T * K)) * (s_p[i * G] / (double)T);
+    for (int e = 0; e < E; ++e) s += ((double)s_cnt[e] / ((double)T * K)) * (s_p[e] / (double)T);
     *aux = (float)((double)E * s);
   }
-  block_scan(hist, base, cnt_out, s_cnt, E, nblk);
-  __syncthreads();
-  segments(s_cnt, seg, E, C);
+  if (wave == 0) {
+    // segments from the counts (E <= 256: lane l holds experts 4l .. 4l+3)
+    int kept4[4], run = 0, drop = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      const int c = e < E ? s_cnt[e] : 0;
+      kept4[i] = min(c, C);
+      drop += c - kept4[i];
+      run += kept4[i];
+    }
+    const int incl = wave_inclusive_scan(run);
+    int off = incl - run;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        seg[e] = off;
+        seg[E + 1 + e] = kept4[i];
+      }
+      off += kept4[i];
+    }
+    const int dropped = wave_sum(drop);
+    if (lane == 63) seg[E] = incl;
+    if (lane == 0) seg[2 * E + 1] = dropped;
+  }
 }
 
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int32_t* base,

@@ -32,7 +32,6 @@ struct RouteArgs {
   const void* x;
   const void* w_r;
   const float* bias;
-  void* wT;            // bf16 [E_pad][H] scratch (bf16 mode)
   float* logits;
   int32_t* topk_ids;
   float* topk_w;

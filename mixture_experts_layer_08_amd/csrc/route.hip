@@ -11,9 +11,12 @@
 // each wave owns 16 tokens and all experts.  Its x rows stream from HBM
 // straight into the A operand through a ring of register slots, loads issued
 // R-1 MFMA steps ahead so that every wave keeps ~16-32 KiB in flight.  The
-// transposed router weight (wT [E_pad][H]) is staged in LDS chunk by chunk,
-// once per workgroup, double-buffered, and read from there as the B operand
-// by all four waves.  fp32 mode uses plain FMA.
+// router weight W_r [H][E] is staged in LDS as it lies in memory, chunk by
+// chunk ([k][E_pad + 16] rows; a chunk of k rows is one contiguous span of
+// W_r), once per workgroup, double-buffered, and read from there as the B
+// operand by all four waves with transposing LDS reads (ds_read_b64_tr_b16),
+// which hand each lane 8 consecutive k of one expert.  fp32 mode uses plain
+// FMA.
 //
 // The epilogue works on the block's fp32 logits in LDS:
 //   - four lanes per token select the top-k (K rounds of a 4-lane argmax;
@@ -28,18 +31,6 @@
 #include "kernels.h"
 
 namespace moe {
-
-// wT[e][k] = W_r[k][e] for e < E, 0 for E <= e < E_pad.
-__global__ __launch_bounds__(256) void k_transpose_router(const bf16* __restrict__ w_r,
-                                                          bf16* __restrict__ wT, int H, int E,
-                                                          int E_pad) {
-  const size_t n = (size_t)E_pad * H;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const int e = (int)(i / H), k = (int)(i % H);
-    wT[i] = e < E ? w_r[(size_t)k * E + e] : f32_to_bf16(0.0f);
-  }
-}
 
 // Shared epilogue.  s_logit holds the block's fp32 logits, row stride ES.
 // Called by all 256 threads after a barrier that published s_logit.  s_ids
@@ -207,6 +198,19 @@ constexpr int route_kc() { return 8192 / (16 * CT) < 512 ? 8192 / (16 * CT) : 51
 template <int CT>
 constexpr int route_ring() { return CT <= 4 ? 32 : 16; }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Two ds_read_b64_tr_b16 (LDS byte addresses addr and addr_hi) as one
+// 8-value fragment.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(uint32_t addr, uint32_t addr_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr_hi);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Buffer-descriptor word 3 for raw 32-bit-indexed loads, and an offset past
 // any descriptor size used here (reads as zero).
 constexpr int kBufferFormat = 0x00020000;
@@ -214,19 +218,19 @@ constexpr uint32_t kOffsetOob = 0x80000000u;
 
 template <int CT>
 __global__ __launch_bounds__(256) void k_route_bf16(
-    const bf16* __restrict__ x, const bf16* __restrict__ wT, const float* __restrict__ bias,
+    const bf16* __restrict__ x, const bf16* __restrict__ w_r, const float* __restrict__ bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, float* __restrict__ psum, int32_t* __restrict__ lrank, int T,
     int H, int E, int K, int nblk, RouterNoise nz) {
   extern __shared__ __attribute__((aligned(16))) float s_logit[];
   __shared__ int32_t s_ids[kRouteBlock * 8];
   __shared__ unsigned long long s_mask[256];
-  constexpr int EP = 16 * CT;            // padded experts (rows of wT)
-  constexpr int KC = route_kc<CT>();     // k per weight chunk
+  constexpr int EP = 16 * CT;            // padded experts (columns of a weight buffer)
+  constexpr int KC = route_kc<CT>();     // k per weight chunk (rows of a buffer)
   constexpr int SPC = KC / 32;           // MFMA steps per chunk
-  constexpr int WROW = KC + 8;           // LDS row stride (elements): 16-byte pad
-  constexpr int WBUF = EP * WROW;        // elements per weight buffer
-  constexpr int WVEC = EP * KC / 8;      // 16-byte vectors per chunk
+  constexpr int EPS = EP + 16;           // LDS row stride (elements): 32-byte pad
+  constexpr int WBUF = KC * EPS;         // elements per weight buffer
+  constexpr int WVEC = EP * KC / 8;      // 16-byte vectors per chunk, at most
   constexpr int WPT = WVEC / 256;        // per thread
   constexpr int R = route_ring<CT>();    // x ring slots (MFMA steps in flight)
   static_assert(WVEC % 256 == 0 && R % SPC == 0, "route tiling");
@@ -269,44 +273,77 @@ __global__ __launch_bounds__(256) void k_route_bf16(
         s < nchunks * SPC && ks * 32 + kg < H ? xoff + (uint32_t)ks * 64 : kOffsetOob;
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0));
   };
-  // weight chunk c: thread's vectors v = tid + 256 q -> row v / (KC/8),
-  // 8-element piece v % (KC/8); zero past H (H is a multiple of 8)
+  // Weight chunk c covers k rows [kc0, kc0 + kn) of W_r, kc0 the chunk's
+  // first k in this workgroup's rotated order: elements kc0 E .. (kc0 + kn) E
+  // of W_r, contiguous (kn E is a multiple of 8 and the span starts 16-byte
+  // aligned).  Thread vectors v = tid + 256 q hold elements 8v .. 8v+7 of the
+  // span, which wstore puts at row k - kc0, column e of the buffer: one
+  // 16-byte write when E is a multiple of 8 (the 8 values are one row's),
+  // else value by value.  Columns E .. EPS-1 only feed logits that are never
+  // stored.  Rows past kn keep the weights of an earlier chunk, or the zeros
+  // both buffers start with: finite values that multiply zero columns of x
+  // (an offset past H reads as zero), so they add nothing.
   const __amdgpu_buffer_rsrc_t wrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wT, (short)0, EP * H * 2, kBufferFormat);
+      __builtin_amdgcn_make_buffer_rsrc((void*)w_r, (short)0, H * E * 2, kBufferFormat);
   u32x4 wreg[WPT];
+  auto chunk_k0 = [&](int c) { return ((c + rc) % nchunks) * KC; };
   auto wload = [&](int c) {
+    const int n = min(KC, H - chunk_k0(c)) * E;  // elements in the span
+    const uint32_t span = (uint32_t)chunk_k0(c) * E * 2;
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       const int v = tid + 256 * q;
-      const int r = v / (KC / 8), p = v % (KC / 8);
-      const int k = ((c + rc) % nchunks) * KC + p * 8;
-      const uint32_t off = k < H ? (uint32_t)(r * H + k) * 2 : kOffsetOob;
+      const uint32_t off = 8 * v < n ? span + (uint32_t)v * 16 : kOffsetOob;
       wreg[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
     }
   };
-  auto wstore = [&](int buf) {
+  const bool e_vec = (E & 7) == 0;
+  auto wstore = [&](int buf, int c) {
+    const int n = min(KC, H - chunk_k0(c)) * E;
+    bf16* wb = wbuf + buf * WBUF;
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
-      const int v = tid + 256 * q;
-      const int r = v / (KC / 8), p = v % (KC / 8);
-      *(u32x4*)(wbuf + buf * WBUF + r * WROW + p * 8) = wreg[q];
+      const int f = 8 * (tid + 256 * q);
+      if (f < n) {
+        int k = f / E, e = f - k * E;
+        if (e_vec) {
+          *(u32x4*)(wb + k * EPS + e) = wreg[q];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t w = wreg[q][i >> 1];
+            wb[k * EPS + e] = __builtin_bit_cast(bf16, (uint16_t)(i & 1 ? w >> 16 : w & 0xffffu));
+            if (++e == E) {
+              e = 0;
+              ++k;
+            }
+          }
+        }
+      }
     }
   };
+  // zero both buffers once: no stale LDS bits (possibly NaN) in rows past kn
+  for (int i = tid; i < 2 * WBUF / 8; i += 256) *(u32x4*)(wbuf + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
 
   f32x4 acc[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 ring[R];
   wload(0);
-  wstore(0);
+  wstore(0, 0);
 #pragma unroll
   for (int i = 0; i < R - 1; ++i) ring[i] = xload(i);
   if (nchunks > 1) wload(1);
   __syncthreads();
-  // B fragment of tile ct at step s_in of a chunk: row ct*16 + lane%16,
-  // 8 k from s_in*32 + 8*(lane/16).  The 16-byte row pad makes the 16 rows
-  // of one read fall in distinct banks.
-  const int b_off = (lane & 15) * WROW + kg;
+  // B fragment of tile ct at step s_in of a chunk: expert ct*16 + lane%16,
+  // 8 k from s_in*32 + 8*(lane/16), by two transposing reads.  In each
+  // 16-lane group, lane i gives the address of 4 consecutive experts
+  // (columns ct*16 + 4 (i%4) ..) of row k0 + i/4 and receives column
+  // ct*16 + i of that 4 x 16 block: 4 consecutive k; the second read takes
+  // rows k0 + 4 ...  The 32-byte row pad puts the 4 rows of a read in
+  // distinct banks.
+  const int b_off = (kg + ((lane & 15) >> 2)) * EPS + 4 * (lane & 3);
   // Whole groups of R steps: steps past the last one multiply zero rows of x.
   for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
@@ -317,16 +354,18 @@ __global__ __launch_bounds__(256) void k_route_bf16(
       // steps past the last chunk read the last chunk's buffer (finite
       // weights times zero rows of x): the other buffer may never have been
       // written, and stale LDS bits could be NaN
-      const bf16* wb = wbuf + (min(c, nchunks - 1) & 1) * WBUF + (((i % SPC) + ri) & (SPC - 1)) * 32 + b_off;
+      const bf16* wb = wbuf + (min(c, nchunks - 1) & 1) * WBUF +
+                       (((i % SPC) + ri) & (SPC - 1)) * 32 * EPS + b_off;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const bf16x8 b = *(const bf16x8*)(wb + ct * 16 * WROW);
+        const uint32_t a0 = (uint32_t)(uintptr_t)(wb + ct * 16);
+        const bf16x8 b = lds_read_tr_pair(a0, a0 + 4 * EPS * 2);
         acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[i], b, acc[ct], 0, 0, 0);
       }
       if ((i + 1) % SPC == 0 && c + 1 < nchunks) {  // uniform over the workgroup
         // chunk c done: publish chunk c+1 into the other buffer, whose last
         // reads (chunk c-1) every wave finished before the previous barrier
-        wstore((c + 1) & 1);
+        wstore((c + 1) & 1, c + 1);
         __syncthreads();
         if (c + 2 < nchunks) wload(c + 2);
       }
@@ -425,12 +464,12 @@ size_t route_lds_bytes(int E) { return (size_t)kRouteBlock * (E | 1) * sizeof(fl
 // larger (they share the space).
 template <int CT>
 static size_t route_bf16_lds_bytes(int E) {
-  const size_t wbufs = 2 * (size_t)(16 * CT) * (route_kc<CT>() + 8) * 2;
+  const size_t wbufs = 2 * (size_t)route_kc<CT>() * (16 * CT + 16) * 2;
   return std::max(wbufs, route_lds_bytes(E));
 }
 
 // Column tiles of 16 experts for the bf16 router: a power of two from 1 to 16
-// (rows of wT beyond E are zero and their logits are never stored).
+// (weight rows beyond E are zero and their logits are never stored).
 int route_col_tiles(int E) {
   const int ct = (E + 15) / 16;
   return ct <= 1 ? 1 : ct <= 2 ? 2 : ct <= 4 ? 4 : ct <= 8 ? 8 : 16;
@@ -443,7 +482,7 @@ static hipError_t launch_route_bf16(const RouteArgs& a, int nblk, hipStream_t st
     const hipError_t err = allow_dynamic_lds<k_route_bf16<CT>>();
     if (err != hipSuccess) return err;
   }
-  k_route_bf16<CT><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.wT, a.bias, a.logits,
+  k_route_bf16<CT><<<nblk, 256, lds, st>>>((const bf16*)a.x, (const bf16*)a.w_r, a.bias, a.logits,
                                            a.topk_ids, a.topk_w, a.hist, a.psum, a.lrank, a.T,
                                            a.H, a.E, a.K, nblk, a.noise);
   return hipGetLastError();
@@ -466,14 +505,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
                                         a.lrank, a.T, a.H, a.E, a.K, nblk, a.noise);
     return hipGetLastError();
   }
-  const int CTp = route_col_tiles(a.E);
-  {
-    const size_t n = (size_t)CTp * 16 * a.H;
-    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
-    k_transpose_router<<<grid, 256, 0, st>>>((const bf16*)a.w_r, (bf16*)a.wT, a.H, a.E,
-                                             CTp * 16);
-  }
-  switch (CTp) {
+  switch (route_col_tiles(a.E)) {
     case 1: return launch_route_bf16<1>(a, nblk, st);
     case 2: return launch_route_bf16<2>(a, nblk, st);
     case 4: return launch_route_bf16<4>(a, nblk, st);

@@ -333,11 +333,11 @@ def test_combine_of_permuted_rows_is_identity():
 
 
 def test_workspace_garbage_and_reuse():
-    """The router's last workgroup computes the permutation's block scan, found
-    through a ticket word in the workspace that no call clears: a workspace
-    full of garbage (all-ones bytes, then random bytes) and one workspace
-    reused over several forwards of different routings must all give the
-    oracle's row map."""
+    """Everything the calls of one forward pass through the workspace (block
+    histograms, ranks, the block scan and segments of moe_aux_loss) is
+    written before it is read in every call: a workspace full of garbage
+    (all-ones bytes, then random bytes) and one workspace reused over several
+    forwards of different routings must all give the oracle's row map."""
     w = Workload("ws_reuse", T=1500, H=64, E=6, K=2, h=64, cf=1.1, bias="normal")
     buf = layer.MoeBuffers.allocate(w)
     gen = torch.Generator(device="cuda").manual_seed(1)
