@@ -464,6 +464,30 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
                                 const void* w_router, void* dx, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/*
+ * moe_forward_noalloc - the whole forward (moe_route, moe_aux_loss,
+ * moe_permute, moe_expert_ffn, moe_combine, in that order, on `stream`) in
+ * one call that allocates nothing, for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The arguments are those of the five calls (same meaning,
+ * layout and ownership); the workspace is instead a static device array of
+ * 16 MiB inside the library, one per GPU, held until the process ends.
+ * Nothing in it needs clearing.  Calls that overlap on one GPU (other
+ * streams, other host threads) share that array and race: serialise them.
+ * Returns MOE_ERR_WORKSPACE when moe_workspace_size(s) exceeds 16 MiB,
+ * MOE_ERR_UNSUPPORTED with MOE_FLAG_TRAIN (training keeps pre-activations in
+ * the workspace), and the five calls' argument errors, all before any launch;
+ * MOE_ERR_HIP if a launch or the array's address lookup fails.
+ */
+moe_status moe_forward_noalloc(const moe_shape* s, const void* x, const void* w_router,
+                               const float* b_router, const void* w1, const void* w2,
+                               const void* ws1, const void* ws2, float* logits,
+                               int32_t* topk_ids, float* topk_w, float* aux, int32_t* counts,
+                               int32_t* kept, int32_t* offsets, int32_t* row_of,
+                               int32_t* token_of, int32_t* n_dropped, void* xp, void* hbuf,
+                               void* out, void* hshared, void* shared_out, void* y,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_expert_ffn_backward", "moe_permute_backward", "moe_mx_operand_scale_bytes",
     "moe_mx_weight_code_bytes",
     "moe_quantize_weights_mxfp8", "moe_permute_mxfp8", "moe_expert_ffn_mxfp8",
-    "moe_combine_mxfp8",
+    "moe_combine_mxfp8", "moe_forward_noalloc",
 )
 
 
@@ -125,6 +125,8 @@ def lib():
         L.moe_expert_ffn_mxfp8.argtypes = [_SHAPE] + [_P] * 21 + [_P]
         L.moe_combine_mxfp8.restype = ctypes.c_int
         L.moe_combine_mxfp8.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [_SHAPE] + [_P] * 23 + [_P]
         _lib = L
     return _lib
 
@@ -277,3 +279,14 @@ def moe_combine_mxfp8(s, out_q, out_s, row_of, topk_w, sh_q, sh_s, y, stream=Non
     _check("moe_combine_mxfp8", lib().moe_combine_mxfp8(
         ctypes.byref(s), _ptr(out_q), _ptr(out_s), _ptr(row_of), _ptr(topk_w), _ptr(sh_q),
         _ptr(sh_s), _ptr(y), _stream(stream)))
+
+
+def moe_forward_noalloc(s, x, w_router, b_router, w1, w2, ws1, ws2, logits, topk_ids, topk_w,
+                        aux, counts, kept, offsets, row_of, token_of, n_dropped, xp, hbuf, out,
+                        hshared, shared_out, y, stream=None):
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w1), _ptr(w2),
+        _ptr(ws1), _ptr(ws2), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(aux),
+        _ptr(counts), _ptr(kept), _ptr(offsets), _ptr(row_of), _ptr(token_of),
+        _ptr(n_dropped), _ptr(xp), _ptr(hbuf), _ptr(out), _ptr(hshared), _ptr(shared_out),
+        _ptr(y), _stream(stream)))

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 #include "mx.h"
@@ -729,3 +731,86 @@ moe_status check_mx_shape(const moe_shape* s) {
   return MOE_OK;
 }
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the five calls with the workspace in a static
+// device array (for callers that cannot allocate).
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kStaticWsBytes = (size_t)16 << 20;
+
+// The workspace of moe_forward_noalloc.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code this name is only a
+// stand-in: its device address on the current device comes from
+// hipGetSymbolAddress (static_ws_ptr), and only that address is ever given to
+// a kernel.  Nothing in it needs to start at zero: every region a call reads
+// (block histograms, softmax partials and ranks from moe_route; block bases,
+// counts and segments from moe_aux_loss) is written earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
+std::mutex g_static_ws_mu;
+void* g_static_ws[64];
+
+// scratch's address on the current device, looked up once per device with
+// that device current.
+hipError_t static_ws_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_static_ws_mu);
+  if (!g_static_ws[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_static_ws[dev] = p;
+  }
+  *out = g_static_ws[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_forward_noalloc(
+    const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+    const void* w1, const void* w2, const void* ws1, const void* ws2, float* logits,
+    int32_t* topk_ids, float* topk_w, float* aux, int32_t* counts, int32_t* kept,
+    int32_t* offsets, int32_t* row_of, int32_t* token_of, int32_t* n_dropped, void* xp,
+    void* hbuf, void* out, void* hshared, void* shared_out, void* y, void* stream) {
+  moe_status st = moe_check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->flags & MOE_FLAG_TRAIN) return MOE_ERR_UNSUPPORTED;
+  // every argument the five calls check, checked before the first launch
+  const bool lin = (s->flags & MOE_FLAG_LOGITS_IN) != 0;
+  const bool shared = s->h_shared > 0;
+  const void* need_ptr[] = {x, w1, w2, logits, topk_ids, topk_w, aux, counts, kept, offsets,
+                            row_of, token_of, n_dropped, xp, hbuf, out, y};
+  for (const void* p : need_ptr)
+    if (!p) return MOE_ERR_INVALID_ARG;
+  const void* need16[] = {x, w1, w2, xp, hbuf, out, y};
+  for (const void* p : need16)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (!lin && (!w_router || !aligned16(w_router))) return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    const void* sh[] = {ws1, ws2, hshared, shared_out};
+    for (const void* p : sh)
+      if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  if (ws_layout(s).total > kStaticWsBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (static_ws_ptr(&ws) != hipSuccess) return MOE_ERR_HIP;
+  if ((st = moe_route(s, x, w_router, b_router, logits, topk_ids, topk_w, ws, kStaticWsBytes,
+                      stream)) != MOE_OK)
+    return st;
+  if ((st = moe_aux_loss(s, ws, kStaticWsBytes, aux, stream)) != MOE_OK) return st;
+  if ((st = moe_permute(s, x, topk_ids, ws, kStaticWsBytes, counts, kept, offsets, row_of,
+                        token_of, n_dropped, xp, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_expert_ffn(s, xp, offsets, w1, w2, hbuf, out, x, ws1, ws2, hshared, shared_out,
+                           ws, kStaticWsBytes, stream)) != MOE_OK)
+    return st;
+  return moe_combine(s, out, row_of, topk_w, shared_out, y, stream);
+}
