@@ -10,9 +10,13 @@ cf-1.com page "Dissecting the MoE communication bottleneck", section 2.2).
 Prints one JSON line: tokens/s of the whole forward, the roofline of the
 dominant kernel (the grouped GEMM, timed with HIP events on its launch stream
 over the timed region), permute / combine / router bandwidth, and the CPU
-oracle timed on a bounded sample of the same workload.  A ``backward`` object
-reports the training step of the same workload separately (a MOE_FLAG_TRAIN
-forward, then the four backward calls); the headline value stays the forward.
+oracle (one warm-up, the median of three runs; the large workloads' FFN
+extrapolated from a 2048-token sample).  Other objects on the same line: the
+other workloads and one GPU's share under 8-way expert parallelism
+(``configs``), the MXFP8 forward (``mxfp8``), the training step
+(``backward``: a MOE_FLAG_TRAIN forward, then the four backward calls), the
+noisy router and the pages' dense-FFN sanity ratio.  The headline value
+stays the bf16 forward.
 """
 
 from __future__ import annotations
@@ -41,7 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads and the EP-8 one-GPU share")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training-step (forward + backward) leg")
@@ -73,30 +79,75 @@ def traffic_from_profile(workload: str, kernel: str = "bf16"):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, p, n_tokens: int):
-    """The oracle, as it stands, on the first n_tokens tokens of the workload."""
+def _median_time(fn, runs: int = 3) -> float:
+    """One untimed warm-up call, then the median wall time of `runs` calls."""
+    fn()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(sorted(ts)[len(ts) // 2])
+
+
+def cpu_baseline(w, p, dev, n_sample: int = 2048, runs: int = 3):
+    """The oracle, as it stands, timed on the host's cores: one warm-up, then
+    the median of `runs` runs.
+
+    The small workloads (tiny_fp32, small_bf16) run the whole float64 oracle
+    forward.  The large ones (mixtral_bf16, finegrained_bf16, skewed_bf16)
+    run the oracle's routing and row map over all T tokens, and the expert
+    FFN plus combine on a seeded sample of `n_sample` tokens; their rate
+    is extrapolated to T (labelled "extrapolated").  The headline value is
+    the bench workload's."""
     import numpy as np
     import threadpoolctl
     import torch
 
+    from mixture_experts_layer_08_amd.inputs import WORKLOADS, make_inputs, sample_tokens
     from oracle import moe_oracle as O
 
-    n = min(n_tokens, w.T)
-    f = lambda t: None if t is None else t.detach().cpu().to(torch.float32).numpy()
-    x = f(p["x"][:n])
-    wr, br = f(p["w_r"]), f(p["b_r"])
-    w1, w2, ws1, ws2 = f(p["w1"]), f(p["w2"]), f(p["ws1"]), f(p["ws2"])
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    O.forward(x, wr, br, w1, w2, ws1, ws2, K=w.K, cf=w.cf)
-    dt = time.perf_counter() - t0
+    f = lambda t: None if t is None else t.detach().cpu().to(torch.float32).numpy()
+    per = {}
+    for name in ("tiny_fp32", "small_bf16", "mixtral_bf16", "finegrained_bf16", "skewed_bf16"):
+        wl = WORKLOADS[name]
+        pp = p if name == w.name else make_inputs(wl, seed=0, device=dev)
+        x, wr, br = f(pp["x"]), f(pp["w_r"]), f(pp["b_r"])
+        w1, w2, ws1, ws2 = f(pp["w1"]), f(pp["w2"]), f(pp["ws1"]), f(pp["ws2"])
+        if name in ("tiny_fp32", "small_bf16"):
+            t = _median_time(lambda: O.forward(x, wr, br, w1, w2, ws1, ws2, K=wl.K, cf=wl.cf),
+                             runs)
+            per[name] = {"tokens_per_s": wl.T / t, "median_s": t, "runs": runs,
+                         "how": "whole oracle forward"}
+        else:
+            def route_all():
+                l = O.router_logits(x, wr, br).astype(np.float32).astype(np.float64)
+                return O.route(l, wl.E, wl.K, wl.cf)
+
+            t_route = _median_time(route_all, runs)
+            r = route_all()
+            toks = sample_tokens(wl.T, n_sample, seed=2).numpy()
+            t_ffn = _median_time(lambda: O.forward_tokens(x, w1, w2, ws1, ws2, r, toks), runs)
+            t_all = t_route + t_ffn * wl.T / len(toks)
+            per[name] = {"tokens_per_s": wl.T / t_all, "extrapolated": True,
+                         "route_median_s": t_route, "ffn_combine_sample_median_s": t_ffn,
+                         "sample_tokens": int(len(toks)), "runs": runs,
+                         "how": (f"router GEMM, routing and row map over all {wl.T} tokens, "
+                                 f"plus expert FFN and combine of {len(toks)} sampled tokens "
+                                 f"scaled to {wl.T}")}
+        del x, w1, w2, ws1, ws2
+        if name != w.name:
+            del pp
+            torch.cuda.empty_cache()
+    head = per.get(w.name)
     return {
-        "value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-        "sample": (f"first {n} of {w.T} tokens of the same workload through the whole float64 "
-                   f"numpy oracle forward (router, routing with capacity on the sub-batch, "
-                   f"expert FFN, combine) in {dt:.1f} s; BLAS threads {threads}, "
-                   f"host cpu_count {os.cpu_count()}"),
+        "value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{w.name}: " + head["how"] + f"; one warm-up then the median of {runs} runs; "
+                   f"BLAS threads {threads}, host cpu_count {os.cpu_count()}"),
+        "extrapolated": bool(head.get("extrapolated", False)),
+        "configs": per,
     }
 
 
@@ -305,6 +356,147 @@ def backward_leg(w, p, dev, steps: int, warmup: int, alpha: float) -> dict:
     }
 
 
+def time_forward(w, p, dev, steps: int, warmup: int, buf=None) -> dict:
+    """The five calls of the forward, `warmup` untimed steps then `steps`
+    timed ones; each call bracketed by HIP events on the launch stream.
+    Returns per-stage mean times, the wall time per step, and the roofline
+    figures of the grouped GEMM and the bandwidth-bound stages."""
+    import torch
+
+    from mixture_experts_layer_08_amd import counters, layer
+
+    buf = buf or layer.MoeBuffers.allocate(w, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward(buf, p, stream)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [[ev() for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        m = marks[s]
+        m[0].record(stream)
+        layer.route(buf, p, stream)
+        m[1].record(stream)
+        layer.aux_loss(buf, stream)
+        m[2].record(stream)
+        layer.permute(buf, p, stream)
+        m[3].record(stream)
+        layer.expert_ffn(buf, p, stream)
+        m[4].record(stream)
+        layer.combine(buf, stream)
+        m[5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def stage_ms(i):
+        return sum(marks[s][i].elapsed_time(marks[s][i + 1]) for s in range(steps)) / steps
+
+    route_ms, aux_ms, perm_ms, ffn_ms, comb_ms = (stage_ms(i) for i in range(5))
+    ms_step = wall * 1e3 / steps
+    N = int(buf.offsets[-1].item())
+    b = 2 if w.dtype == "bf16" else 4
+    launches = 2 + (2 if w.hs else 0)
+    flop_step = 2 * counters.grouped_gemm_flop_per_launch(N, w.H, w.h)
+    if w.hs:
+        flop_step += 2 * counters.grouped_gemm_flop_per_launch(w.T, w.H, w.hs)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flop_step / (ffn_ms * 1e-3) / 1e12
+    kept = buf.kept.cpu().tolist()
+    t_f, t_b, t_seg = counters.segment_roofline_s(kept, w.H, w.h, b, peak * 1e12,
+                                                  PEAK_HBM_GBS * 1e9, w.T if w.hs else 0, w.hs)
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    perm_bytes = counters.permute_bytes(w.T, N, w.H, b, w.K)
+    comb_bytes = counters.combine_kernel_bytes(w.T, N, w.H, b, w.K, bool(w.hs))
+    route_bytes = counters.router_bytes(w.T, w.H, w.E, w.K, b)
+    return {
+        "buf": buf, "N": N, "ms_step": ms_step, "tokens_per_s": w.T / (ms_step * 1e-3),
+        "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute": perm_ms,
+                      "expert_ffn": ffn_ms, "combine": comb_ms},
+        "gemm": {"achieved": achieved, "peak": peak, "frac": achieved / peak,
+                 "flop_per_launch": flop_step / launches, "avg_launch_ms": ffn_ms / launches},
+        "expert_ffn_roofline": {"flop_bound_ms": t_f * 1e3, "byte_bound_ms": t_b * 1e3,
+                                "segment_bound_ms": t_seg * 1e3, "measured_ms": ffn_ms,
+                                "frac_of_segment_bound": t_seg * 1e3 / ffn_ms},
+        "hbm": {
+            "permute": {"GB/s": gbs(perm_bytes, perm_ms),
+                        "frac": gbs(perm_bytes, perm_ms) / PEAK_HBM_GBS, "bytes": perm_bytes},
+            "combine": {"GB/s": gbs(comb_bytes, comb_ms),
+                        "frac": gbs(comb_bytes, comb_ms) / PEAK_HBM_GBS, "bytes": comb_bytes},
+            "route": {"GB/s": gbs(route_bytes, route_ms),
+                      "frac": gbs(route_bytes, route_ms) / PEAK_HBM_GBS, "bytes": route_bytes},
+        },
+    }
+
+
+def configs_leg(w_main, dev, steps: int, warmup: int) -> dict:
+    """The other workloads, each timed as the headline one (fewer steps), and
+    the expert FFN of one GPU's share under 8-way expert parallelism at the
+    headline shape: one expert's segment of T*K rows (65536 at T=32768,
+    top-2), H x h_exp, through the same grouped GEMM."""
+    import torch
+
+    from mixture_experts_layer_08_amd import binding as B
+    from mixture_experts_layer_08_amd import counters
+    from mixture_experts_layer_08_amd.inputs import WORKLOADS, make_inputs
+
+    out = {}
+    for name in ("tiny_fp32", "small_bf16", "mixtral_bf16", "finegrained_bf16", "skewed_bf16"):
+        if name == w_main.name:
+            continue
+        wl = WORKLOADS[name]
+        p = make_inputs(wl, seed=0, device=dev)
+        r = time_forward(wl, p, dev, steps, warmup)
+        out[name] = {
+            "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_step"],
+            "kept_rows": r["N"], "stages_ms": r["stages_ms"],
+            "grouped_gemm_frac_of_peak": r["gemm"]["frac"],
+            "grouped_gemm_tflops": r["gemm"]["achieved"],
+            "frac_of_segment_bound": r["expert_ffn_roofline"]["frac_of_segment_bound"],
+            "segment_bound_ms": r["expert_ffn_roofline"]["segment_bound_ms"],
+            "hbm_frac": {k: v["frac"] for k, v in r["hbm"].items()},
+        }
+        del r, p
+        torch.cuda.empty_cache()
+
+    # EP-8 one-GPU share: a single segment of T*K rows through moe_expert_ffn
+    wm = WORKLOADS["mixtral_bf16"]
+    rows = wm.T * wm.K
+    s = B.make_shape(rows, wm.H, 1, 1, wm.h, 0, 0.0, B.MOE_BF16)
+    g = torch.Generator(device=dev).manual_seed(0)
+    xp = (torch.randn((rows, wm.H), generator=g, device=dev)).to(torch.bfloat16)
+    w1 = (torch.randn((1, wm.H, wm.h), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((1, wm.h, wm.H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    offsets = torch.tensor([0, rows], dtype=torch.int32, device=dev)
+    hbuf = torch.empty((rows, wm.h), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((rows, wm.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((B.moe_workspace_size(s),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    call = lambda: B.moe_expert_ffn(s, xp, offsets, w1, w2, hbuf, o, None, None, None, None,
+                                    None, ws, stream)
+    for _ in range(2):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n = 5
+    ev[0].record(stream)
+    for _ in range(n):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / n
+    flop = 2 * counters.grouped_gemm_flop_per_launch(rows, wm.H, wm.h)
+    tf = flop / (ms * 1e-3) / 1e12
+    out["ep8_share_mixtral"] = {
+        "rows": rows, "H": wm.H, "h_exp": wm.h, "expert_ffn_ms": ms, "tflops": tf,
+        "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+        "note": "one GPU's expert FFN under 8-way expert parallelism at T=32768, top-2: "
+                "one expert, one segment of T*K rows (GEMM1 + GELU, GEMM2); no all-to-all"}
+    del xp, w1, w2, hbuf, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -324,69 +516,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = make_inputs(w, seed=a.seed, device=dev)
-    buf = layer.MoeBuffers.allocate(w, device=dev)
-    stream = torch.cuda.current_stream()
-
-    for _ in range(a.warmup):
-        layer.forward(buf, p, stream)
-    torch.cuda.synchronize()
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    marks = [[ev() for _ in range(6)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(a.steps):
-        m = marks[s]
-        m[0].record(stream)
-        layer.route(buf, p, stream)
-        m[1].record(stream)
-        layer.aux_loss(buf, stream)
-        m[2].record(stream)
-        layer.permute(buf, p, stream)
-        m[3].record(stream)
-        layer.expert_ffn(buf, p, stream)
-        m[4].record(stream)
-        layer.combine(buf, stream)
-        m[5].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    def stage_ms(i):
-        return sum(marks[s][i].elapsed_time(marks[s][i + 1]) for s in range(a.steps)) / a.steps
-
-    route_ms, aux_ms, perm_ms, ffn_ms, comb_ms = (stage_ms(i) for i in range(5))
-    ms_step = wall * 1e3 / a.steps
-    N = int(buf.offsets[-1].item())
+    r = time_forward(w, p, dev, a.steps, a.warmup)
+    buf, N, ms_step = r["buf"], r["N"], r["ms_step"]
     dropped = int(buf.n_dropped.item())
-    b = 2 if w.dtype == "bf16" else 4
-
     # dominant kernel: the grouped GEMM, launched twice per step (GEMM1 with
     # GELU, GEMM2) plus twice more for the shared expert when present
-    launches = 2 + (2 if w.hs else 0)
-    gemm_flop_step = 2 * counters.grouped_gemm_flop_per_launch(N, w.H, w.h)
-    if w.hs:
-        gemm_flop_step += 2 * counters.grouped_gemm_flop_per_launch(w.T, w.H, w.hs)
-    flop_per_launch = gemm_flop_step / launches
-    launch_s = ffn_ms * 1e-3 / launches
-    achieved = flop_per_launch / launch_s / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    gm = r["gemm"]
     traffic = traffic_from_profile(w.name)
-
-    # the expert FFN against its roofline, segment by segment: a segment of a
-    # few hundred rows is bound by reading its weights, not by MFMA
-    kept = buf.kept.cpu().tolist()
-    t_f, t_b, t_seg = counters.segment_roofline_s(kept, w.H, w.h, b, peak * 1e12,
-                                                  PEAK_HBM_GBS * 1e9, w.T if w.hs else 0, w.hs)
-    ffn_roofline = {"flop_bound_ms": t_f * 1e3, "byte_bound_ms": t_b * 1e3,
-                    "segment_bound_ms": t_seg * 1e3, "measured_ms": ffn_ms,
-                    "frac_of_segment_bound": t_seg * 1e3 / ffn_ms,
-                    "note": "segment bound: sum over expert segments of max(FLOP / MFMA peak, "
-                            "(weights + activations) bytes / HBM peak)"}
-
-    perm_bytes = counters.permute_bytes(w.T, N, w.H, b, w.K)
-    comb_bytes = counters.combine_kernel_bytes(w.T, N, w.H, b, w.K, bool(w.hs))
-    route_bytes = counters.router_bytes(w.T, w.H, w.E, w.K, b)
-    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    ffn_roofline = dict(r["expert_ffn_roofline"],
+                        note="segment bound: sum over expert segments of max(FLOP / MFMA peak, "
+                             "(weights + activations) bytes / HBM peak)")
+    hbm = r["hbm"]
+    hbm["permute"]["note"] = "moe_permute: one kernel (row map and copy)"
+    hbm["route"]["note"] = "moe_route: one kernel (router GEMM, softmax, top-k, block partials)"
+    hbm["aux_loss_ms"] = r["stages_ms"]["aux_loss"]
 
     res = {
         "metric": METRIC,
@@ -406,20 +549,16 @@ def main():
                    "kept_rows": N, "dropped_assignments": dropped,
                    "aux_loss": float(buf.aux.item())},
         "roofline": {"kernel": "k_grouped_gemm_bf16" if w.dtype == "bf16" else "k_grouped_gemm_f32",
-                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "flop_per_launch": flop_per_launch, "avg_launch_ms": launch_s * 1e3},
+                     "bound": "mfma", "achieved": gm["achieved"], "peak": gm["peak"],
+                     "unit": "TFLOP/s", "frac": gm["frac"], "traffic": traffic,
+                     "traffic_note": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, "
+                                     "calibrated on a device copy), from the committed profile "
+                                     "when it matches the kernel source; else null",
+                     "flop_per_launch": gm["flop_per_launch"],
+                     "avg_launch_ms": gm["avg_launch_ms"]},
         "expert_ffn_roofline": ffn_roofline,
-        "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute": perm_ms,
-                      "expert_ffn": ffn_ms, "combine": comb_ms},
-        "hbm": {
-            "permute": {"GB/s": gbs(perm_bytes, perm_ms), "frac": gbs(perm_bytes, perm_ms) / PEAK_HBM_GBS,
-                        "bytes": perm_bytes, "note": "moe_permute: scan, offsets and copy kernels"},
-            "combine": {"GB/s": gbs(comb_bytes, comb_ms), "frac": gbs(comb_bytes, comb_ms) / PEAK_HBM_GBS,
-                        "bytes": comb_bytes},
-            "route": {"GB/s": gbs(route_bytes, route_ms), "frac": gbs(route_bytes, route_ms) / PEAK_HBM_GBS,
-                      "bytes": route_bytes},
-        },
+        "stages_ms": r["stages_ms"],
+        "hbm": hbm,
         "cpu_baseline": None,
     }
     if not a.no_side_legs:
@@ -430,6 +569,7 @@ def main():
         torch.cuda.empty_cache()
     if not a.no_backward:
         del buf
+        r.pop("buf", None)
         torch.cuda.empty_cache()
         res["backward"] = backward_leg(w, p, dev, a.backward_steps, min(a.warmup, 3), a.alpha)
     if a.copy_calibration > 0:
@@ -439,8 +579,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if not a.no_configs:
+        res["configs"] = configs_leg(w, dev, min(a.steps, 20), min(a.warmup, 3))
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, p, a.cpu_sample_tokens)
+        res["cpu_baseline"] = cpu_baseline(w, p, dev, a.cpu_sample_tokens)
     print(json.dumps(res))
 
 
