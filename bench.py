@@ -66,8 +66,9 @@ def parse():
 
 
 def traffic_from_profile(workload: str, kernel: str = "bf16"):
-    """HBM bytes per grouped-GEMM launch from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel source; else None."""
+    """L2-miss bytes per grouped-GEMM launch (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a device copy) from the committed rocprofv3 --pmc summary,
+    if it was taken on the current kernel source; else None."""
     stem = "grouped_gemm" if kernel == "bf16" else f"grouped_gemm_{kernel}"
     p = os.path.join(ROOT, "profiles", f"{stem}_{workload}_traffic.json")
     if not os.path.exists(p):
@@ -76,7 +77,7 @@ def traffic_from_profile(workload: str, kernel: str = "bf16"):
     from mixture_experts_layer_08_amd.profiling import gemm_source_hash
     if d.get("gemm_source_sha256_16") != gemm_source_hash(kernel):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("l2_miss_bytes_per_launch")
 
 
 def _median_time(fn, runs: int = 3) -> float:

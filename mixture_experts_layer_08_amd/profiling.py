@@ -1,9 +1,17 @@
-"""Summaries of rocprofv3 counter runs for the roofline's `traffic` figure.
+"""Summaries of rocprofv3 counter runs: the roofline's `traffic` figure, the
+bandwidth-bound kernels' bytes, and the grouped GEMMs' clock and MFMA-busy
+fractions.
 
-HBM traffic of a kernel is read from two `rocprofv3 --pmc` runs (FETCH_SIZE,
-then WRITE_SIZE; both in KiB per dispatch).  Each counter is calibrated with
-a plain device copy of known size profiled in the same run: the factor
-(known bytes) / (counter bytes) scales the kernel's reading.
+Traffic of a kernel is read from two `rocprofv3 --pmc` runs (FETCH_SIZE,
+then WRITE_SIZE; both in KiB per dispatch).  These count the requests that
+miss the L2 (whether the Infinity Cache or HBM then serves them), so the
+figure is L2-miss traffic, an upper bound on HBM bytes.  Each counter is
+calibrated with a plain device copy of known size profiled in the same run:
+the factor (known bytes) / (counter bytes) scales the kernel's reading.  On
+this GPU FETCH_SIZE reports half of the copy's bytes read (factor 2.0) and
+WRITE_SIZE all of its bytes written (1.0); the raw KiB are kept beside the
+scaled bytes, since the copy's loads are plain vector loads and the GEMM's
+are LDS-direct loads.
 
     python -m mixture_experts_layer_08_amd.profiling traffic \
         --fetch <fetch run>/p_counter_collection.csv \
@@ -86,7 +94,10 @@ def traffic(fetch_csv, write_csv, copy_bytes, workload, out, kernel="bf16"):
         res[f"{name}_launches"] = len(gemms)
         res[f"{name}_bytes_per_launch_by_kernel"] = {
             k: sum(v) / len(v) * 1024.0 * factor for k, v in sorted(by_name.items())}
-    res["hbm_bytes_per_launch"] = totals["fetch"] + totals["write"]
+    # FETCH_SIZE + WRITE_SIZE: requests that missed the L2, not HBM bytes
+    res["l2_miss_bytes_per_launch"] = totals["fetch"] + totals["write"]
+    res["l2_miss_bytes_per_launch_unscaled"] = (res["fetch_kib_per_launch_raw"] +
+                                                res["write_kib_per_launch_raw"]) * 1024.0
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -107,9 +118,9 @@ def per_kernel(path: str, counter: str, patterns: dict):
 
 # the bandwidth-bound kernels of the forward (bf16 and MXFP8 forms)
 HBM_KERNELS = {
-    "k_route_bf16": r"k_route_bf16<", "k_transpose_router": r"k_transpose_router",
-    "k_scan_blocks": r"k_scan_blocks", "k_permute": r"k_permute<", "k_permute_mx8": r"k_permute_mx8<",
-    "k_combine": r"k_combine<", "k_combine_mx8": r"k_combine_mx8<",
+    "k_route_bf16": r"k_route_bf16<", "k_aux": r"k_aux\b", "k_permute": r"k_permute<",
+    "k_permute_mx8": r"k_permute_mx8<", "k_combine": r"k_combine<",
+    "k_combine_mx8": r"k_combine_mx8<",
 }
 
 
@@ -142,27 +153,64 @@ def hbm(fetch_csv, write_csv, copy_bytes, title, cmd, out):
     print("\n".join(lines))
 
 
-def mfma(csv_path, title, cmd, out, simds: int = 1024):
-    """Markdown table: per grouped-GEMM dispatch, SQ_VALU_MFMA_BUSY_CYCLES over
-    all SIMDs divided by (SIMDs x GRBM_GUI_ACTIVE per XCD): the fraction of
-    the kernel's cycles the MFMA pipes were busy."""
+def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz: float = 2.4,
+          copy_bytes: int = 1 << 30):
+    """Markdown table of the grouped GEMMs' effective clock and MFMA use,
+    from one `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE ...` run:
+      - effective clock = GRBM_GUI_ACTIVE (shader-clock cycles, summed over
+        the XCDs) / XCDs / the dispatch's duration; the run's calibration
+        copy of copy_bytes, a memory-bound kernel, is listed as the check
+        (it should read about the 2.4 GHz maximum);
+      - MFMA busy per cycle = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / (effective
+        clock x duration), and of the peak clock.  Their product is the
+        fraction of dense MFMA peak."""
     pats = {"k_grouped_gemm_bf16 (GEMM1, GELU)": r"k_grouped_gemm_bf16<\s*0\s*,\s*1>",
             "k_grouped_gemm_bf16 (GEMM2)": r"k_grouped_gemm_bf16<\s*0\s*,\s*0>",
             "k_grouped_gemm_mx8 (GEMM1, GELU)": r"k_grouped_gemm_mx8<1>",
-            "k_grouped_gemm_mx8 (GEMM2)": r"k_grouped_gemm_mx8<0>"}
-    busy, _ = per_kernel(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", pats)
-    gui, _ = per_kernel(csv_path, "GRBM_GUI_ACTIVE", pats)
+            "k_grouped_gemm_mx8 (GEMM2)": r"k_grouped_gemm_mx8<0>",
+            "k_permute (memory-bound)": r"k_permute<",
+            "k_combine (memory-bound)": r"k_combine<"}
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(csv_path)):
+        d = int(r["Dispatch_Id"])
+        per[d]["name"] = r["Kernel_Name"]
+        per[d]["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = {n: [] for n in pats}
+    copies = []
+    for d in sorted(per):
+        v = per[d]
+        if COPY_KERNEL in v["name"]:
+            copies.append(v)
+            continue
+        for n, rx in pats.items():
+            if re.search(rx, v["name"]):
+                rows[n].append(v)
+                break
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
              cmd, "```", "",
-             f"MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over the {simds} SIMDs) / "
-             f"({simds} x GRBM_GUI_ACTIVE / 8), GRBM_GUI_ACTIVE being summed over the 8 XCDs.", "",
-             "| kernel | dispatches | MFMA busy cycles | GUI active cycles (per XCD) | MFMA busy |",
-             "|---|---|---|---|---|"]
-    for n in pats:
-        if busy[n]:
-            b = sum(busy[n]) / len(busy[n])
-            g = sum(gui[n]) / len(gui[n]) / 8.0
-            lines.append(f"| `{n}` | {len(busy[n])} | {b:.4g} | {g:.4g} | {b / (simds * g):.1%} |")
+             f"Effective clock = GRBM_GUI_ACTIVE / {xcds} XCDs / dispatch duration (shader-clock "
+             f"cycles); MFMA busy per cycle = SQ_VALU_MFMA_BUSY_CYCLES / {simds} SIMDs / "
+             f"(clock x duration).  The first dispatch of each kernel is a warm-up and is left "
+             f"out (counter runs serialise dispatches, so their durations run a little long).", "",
+             "| kernel | dispatches | mean us | effective clock GHz | MFMA busy per cycle | "
+             f"clock x busy / {peak_ghz} GHz |", "|---|---|---|---|---|---|"]
+    big = [c for c in copies if c["dur"] > 100e-6]
+    if big:
+        c = max(big, key=lambda c: c["dur"])
+        ghz = c["GRBM_GUI_ACTIVE"] / xcds / c["dur"] / 1e9
+        lines.append(f"| device copy of {copy_bytes >> 20} MiB (check) | 1 | {c['dur'] * 1e6:.1f} | "
+                     f"{ghz:.2f} | - | - |")
+    for n, vs in rows.items():
+        vs = vs[1:] if len(vs) > 1 else vs
+        if not vs:
+            continue
+        dur = sum(v["dur"] for v in vs) / len(vs)
+        ghz = sum(v["GRBM_GUI_ACTIVE"] / xcds / v["dur"] for v in vs) / len(vs) / 1e9
+        mf = sum(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for v in vs) / len(vs) / simds
+        busy = mf / (ghz * 1e9 * dur) if mf else 0.0
+        lines.append(f"| `{n}` | {len(vs)} | {dur * 1e6:.1f} | {ghz:.2f} | "
+                     f"{busy:.1%} | {busy * ghz / peak_ghz:.1%} |")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -230,7 +278,7 @@ def main():
     h.add_argument("--title", required=True)
     h.add_argument("--command", required=True, help="the command that produced the runs")
     h.add_argument("--out", required=True)
-    m = sub.add_parser("mfma")
+    m = sub.add_parser("clock")
     m.add_argument("--csv", required=True)
     m.add_argument("--title", required=True)
     m.add_argument("--command", required=True, help="the command that produced the run")
@@ -256,7 +304,7 @@ def main():
         stats(a.stats, a.trace, a.bench_log, a.title, a.command, a.note, a.out, a.kernel,
               window=win)
     else:
-        mfma(a.csv, a.title, a.command, a.out)
+        clock(a.csv, a.title, a.command, a.out)
 
 
 if __name__ == "__main__":
