@@ -23,6 +23,8 @@
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 
 
@@ -156,6 +158,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // 512-byte row; k rows past the contraction range lie beyond num_records.
   const int c_row0 = (lane >> 5) + 2 * wave;     // (row & 3) is d-invariant
   const int c_chunk = (lane & 31) ^ (4 * (c_row0 & 3));
+  // A rows past the tile's valid rows are not fetched (they read as zero and
+  // their outputs are never stored): a segment's last tile moves only its
+  // own rows.
+  bool a_live[kDma];
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) a_live[d] = kTN || 16 * (8 * d + wave) + r_row_l < rows;
   // A
   u32x4 ra_src;
   uint32_t a_off, a_dstride, a_kstride;
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     if (d < kDma) {
       const uint32_t off = a_off + d * a_dstride + (uint32_t)kt * a_kstride;
       dma_load16(st + (8 * d + wave) * 1024,
-                 kARows ? (k0 + r_chunk * 8 < Kd ? off : kOob) : off, ra_src);
+                 kARows ? (k0 + r_chunk * 8 < Kd && a_live[d] ? off : kOob) : off, ra_src);
     } else {
       const uint32_t off = b_off + (d - kDma) * b_dstride + (uint32_t)kt * b_kstride;
       dma_load16(st + BM2 * BK2 * 2 + (8 * (d - kDma) + wave) * 1024,
@@ -254,39 +262,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Operand fragments of one k-substep (16 k): 4 of A, 2 of B.
-  auto read_ops = [&](uint32_t st, int ks, bf16x8* a, bf16x8* b) {
+  // The loop below is instantiated for NA = 0..4 active 32-row blocks of
+  // the wave's 128 rows: in a segment's last tile the waves skip the MFMAs
+  // and A-fragment reads of rows past the segment (rows form only; TN tiles
+  // always run NA = 4).  Each SIMD holds one wave of each row half, so the
+  // skipped work shortens the tile.  Every instantiation issues the same
+  // LDS-direct loads and barriers.
+  // Operand fragments of one k-substep (16 k): NA of A, 2 of B (none if
+  // NA = 0).
+  auto read_ops = [&](auto na_c, uint32_t st, int ks, bf16x8* a, bf16x8* b) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
       a[i] = kARows ? lds_read_b128(st + a_rd[ks] + i * 32 * BK2 * 2)
                     : lds_read_tr_pair(st + a_rd[i] + ks * 8192, st + a_rd[i] + ks * 8192 + 2048);
+    if (NA > 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = kBRows ? lds_read_b128(st + b_rd[ks] + j * 32 * BK2 * 2)
-                    : lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+      for (int j = 0; j < 2; ++j)
+        b[j] = kBRows ? lds_read_b128(st + b_rd[ks] + j * 32 * BK2 * 2)
+                      : lds_read_tr_pair(st + b_rd[j] + ks * 8192, st + b_rd[j] + ks * 8192 + 2048);
+    }
   };
   // 8 LDS reads (12 with A in cols form) spread between 8 MFMAs (mask 0x008
   // MFMA, 0x100 DS read).
-  auto mma_reads = [&](const bf16x8* a, const bf16x8* b) {
+  auto mma_reads = [&](auto na_c, const bf16x8* a, const bf16x8* b) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 2 * NA; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, kARows ? 1 : (kBRows ? 1 : 2), 0);
     }
   };
   // The last substep's MFMAs with the refill loads of step kt_fill between
-  // them (one after every second MFMA).
-  auto mma_refill = [&](const bf16x8* a, const bf16x8* b, int kt_fill) {
+  // them (one after every second MFMA slot).
+  auto mma_refill = [&](auto na_c, const bf16x8* a, const bf16x8* b, int kt_fill) {
+    constexpr int NA = decltype(na_c)::value;
     const uint32_t st = stage_addr(kt_fill);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int i = t >> 1, j = t & 1;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      if (i < NA)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
       if (t & 1) dma(st, t >> 1, kt_fill);
     }
   };
@@ -313,18 +334,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   }
   wait_vmcnt<(kStages - 2) * 2 * kDma>();  // step 0 landed (own loads)
   block_barrier();                          // ... and every wave's
-  bf16x8 pa[4], pb[2], qa[4], qb[2];
-  read_ops(lds0, 0, pa, pb);
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
-    const uint32_t st1 = lds0 + (uint32_t)((kt + 1) % kStages) * kStageBytes;
-    read_ops(st, 1, qa, qb);
-    mma_reads(pa, pb);
-    wait_vmcnt<(kStages - 3) * 2 * kDma>();
-    wait_lgkm0();
-    block_barrier();
-    read_ops(st1, 0, pa, pb);  // past the last step: harmless reads of a landed stage
-    mma_refill(qa, qb, kt + kStages - 1);  // past K: zeros into a slot never read
+  auto k_loop = [&](auto na_c) {
+    bf16x8 pa[4], pb[2], qa[4], qb[2];
+    read_ops(na_c, lds0, 0, pa, pb);
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint32_t st = lds0 + (uint32_t)(kt % kStages) * kStageBytes;
+      const uint32_t st1 = lds0 + (uint32_t)((kt + 1) % kStages) * kStageBytes;
+      read_ops(na_c, st, 1, qa, qb);
+      mma_reads(na_c, pa, pb);
+      wait_vmcnt<(kStages - 3) * 2 * kDma>();
+      wait_lgkm0();
+      block_barrier();
+      read_ops(na_c, st1, 0, pa, pb);  // past the last step: harmless reads of a landed stage
+      mma_refill(na_c, qa, qb, kt + kStages - 1);  // past K: zeros into a slot never read
+    }
+  };
+  using NA4 = std::integral_constant<int, 4>;
+  if (kTN) {
+    k_loop(NA4{});
+  } else {
+    // active 32-row blocks of this wave (wave-uniform)
+    const int na = __builtin_amdgcn_readfirstlane(min(max((rows - wm * 128 + 31) >> 5, 0), 4));
+    if (na == 4) k_loop(NA4{});
+    else if (na == 3) k_loop(std::integral_constant<int, 3>{});
+    else if (na == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (na == 1) k_loop(std::integral_constant<int, 1>{});
+    else k_loop(std::integral_constant<int, 0>{});
   }
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 

@@ -70,6 +70,46 @@ def test_expert_ffn_alone(dtype, hs):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H,h", [(256, 192), (328, 136)])
+def test_expert_ffn_short_segments(dtype, H, h):
+    """Segments shorter than one 256-row tile, and tails of every length class
+    around the 32-row MFMA blocks and the 128-row halves of a tile: 1, 31, 32,
+    33, 63, 64, 65, 96, 127, 128, 129, 160, 192, 224, 255, 257 and 300 rows.
+    In a segment's last tile the kernel skips the MFMA blocks and A loads of
+    rows past the segment, so every row of every segment is compared, segment
+    by segment, and the rows past the last segment must stay untouched."""
+    sizes = [1, 31, 32, 33, 63, 64, 65, 96, 0, 127, 128, 129, 160, 192, 224, 255, 257, 300]
+    E = len(sizes)
+    N = sum(sizes)
+    # T > N, so the packed buffers have rows past the last segment
+    w = Workload("ffn_short", T=N + 100, H=H, E=E, K=1, h=h, hs=0, cf=0.0, dtype=dtype)
+    p = make_inputs(w, seed=37, device="cuda")
+    buf = layer.MoeBuffers.allocate(w)
+    assert buf.xp.shape[0] == N + 100
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    g = torch.Generator(device="cuda").manual_seed(38)
+    buf.xp.copy_(torch.randn((buf.xp.shape[0], w.H), generator=g, device="cuda").to(buf.xp.dtype))
+    buf.offsets.copy_(torch.from_numpy(offsets))
+    sentinel = torch.full_like(buf.out, 7.0)
+    buf.out.copy_(sentinel)
+    layer.expert_ffn(buf, p)
+    torch.cuda.synchronize()
+    got = f64(buf.out[:N])
+    ref = O.expert_ffn(f64(buf.xp[:N]), offsets, f64(p["w1"]), f64(p["w2"]))
+    scale = max(np.abs(ref).max(), 1e-30)
+    per_seg = {}
+    for e, n in enumerate(sizes):
+        if n == 0:
+            continue
+        a, b = offsets[e], offsets[e + 1]
+        per_seg[n] = float(np.abs(got[a:b] - ref[a:b]).max() / scale)
+    print(f"[ffn short segments {dtype} H={H} h={h}] worst {max(per_seg.values()):.2e}", flush=True)
+    bad = {n: v for n, v in per_seg.items() if not v <= TOL[dtype]}
+    assert not bad, bad
+    assert torch.equal(buf.out[N:], sentinel[N:]), "rows past the last segment were written"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shared", [False, True])
 def test_combine_alone(dtype, shared):
     T, K, H, N = 500, 3, 264, 900
