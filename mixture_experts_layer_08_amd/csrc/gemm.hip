@@ -144,9 +144,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;
   const int rr = lane & 31, kh = lane >> 5;
   const int n0 = nt * BN2;
+  // Wave layout.  Normally 2 (M) x 4 (N): the wave owns rows rbase ..
+  // rbase + 127 and columns cbase .. cbase + 63 of the tile.  A tile with at
+  // most 128 valid columns (the last N-tile of an output whose width is not
+  // a multiple of 256) uses 4 (M) x 2 (N) instead, 64 x 64 per wave: the
+  // waves of the empty half would otherwise multiply zeros, and with waves
+  // dealt to SIMDs in turn (SIMD = wave % 4) all four SIMDs keep work.
+  const bool narrow = !kTN && N - n0 <= BN2 / 2;
+  const int rbase = narrow ? (wave & 3) * 64 : (wave >> 2) * 128;
+  const int cbase = narrow ? (wave >> 2) * 64 : (wave & 3) * 64;
+  const int na_max = narrow ? 2 : 4;  // 32-row blocks the wave owns
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- global -> LDS loaders (2 + 2 instructions per wave per stage) ----
@@ -160,10 +169,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   const int c_chunk = (lane & 31) ^ (4 * (c_row0 & 3));
   // A rows past the tile's valid rows are not fetched (they read as zero and
   // their outputs are never stored): a segment's last tile moves only its
-  // own rows.
+  // own rows.  Likewise the weight columns past N in the row-major form
+  // (which would otherwise read the next k row's first columns).
   bool a_live[kDma];
 #pragma unroll
   for (int d = 0; d < kDma; ++d) a_live[d] = kTN || 16 * (8 * d + wave) + r_row_l < rows;
+  const bool b_live = kBRows || kTN || n0 + c_chunk * 8 < N;
   // A
   u32x4 ra_src;
   uint32_t a_off, a_dstride, a_kstride;
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     } else {
       const uint32_t off = b_off + (d - kDma) * b_dstride + (uint32_t)kt * b_kstride;
       dma_load16(st + BM2 * BK2 * 2 + (8 * (d - kDma) + wave) * 1024,
-                 kBRows ? (k0 + r_chunk * 8 < Kd ? off : kOob) : off, rb_src);
+                 kBRows ? (k0 + r_chunk * 8 < Kd ? off : kOob) : (b_live ? off : kOob), rb_src);
     }
   };
   auto stage_addr = [&](int kt) {
@@ -238,20 +249,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   if (kARows) {
 #pragma unroll
     for (int ks = 0; ks < kSub; ++ks)
-      a_rd[ks] = (uint32_t)(wm * 128 + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
+      a_rd[ks] = (uint32_t)(rbase + rr) * (BK2 * 2) + (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a_rd[i] = cols_addr(wm * 128 + i * 32);
+    for (int i = 0; i < 4; ++i) a_rd[i] = cols_addr(rbase + i * 32);
   }
   uint32_t b_rd[2];
   if (kBRows) {
 #pragma unroll
     for (int ks = 0; ks < kSub; ++ks)
-      b_rd[ks] = BM2 * BK2 * 2 + (uint32_t)(wn * 64 + rr) * (BK2 * 2) +
+      b_rd[ks] = BM2 * BK2 * 2 + (uint32_t)(cbase + rr) * (BK2 * 2) +
                  (uint32_t)(a_swz(rr, 2 * ks + kh) * 16);
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b_rd[j] = BM2 * BK2 * 2 + cols_addr(wn * 64 + j * 32);
+    for (int j = 0; j < 2; ++j) b_rd[j] = BM2 * BK2 * 2 + cols_addr(cbase + j * 32);
   }
 
   f32x16 acc[4][2];
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
     k_loop(NA4{});
   } else {
     // active 32-row blocks of this wave (wave-uniform)
-    const int na = __builtin_amdgcn_readfirstlane(min(max((rows - wm * 128 + 31) >> 5, 0), 4));
+    const int na = __builtin_amdgcn_readfirstlane(min(max((rows - rbase + 31) >> 5, 0), na_max));
     if (na == 4) k_loop(NA4{});
     else if (na == 3) k_loop(std::integral_constant<int, 3>{});
     else if (na == 2) k_loop(std::integral_constant<int, 2>{});
@@ -372,14 +383,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // stores its fp32 groups of 4 directly).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = wm * 128 + i * 32 + rr;
-    if (m >= rows) continue;  // uniform over the lane pair (m, m + 32)
+    const int m = rbase + i * 32 + rr;
+    if (i >= na_max || m >= rows) continue;  // uniform over the lane pair (m, m + 32)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (kTN) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * 64 + j * 32 + 8 * g + 4 * kh;
+          const int n = n0 + cbase + j * 32 + 8 * g + 4 * kh;
           if (n < N) {
             float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
             *(f32x4*)(crow + n) = f32x4{acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
       bf16* crow = (bf16*)Cv;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const int nb = n0 + wn * 64 + j * 32 + 16 * p;  // first column of the pair
+        const int nb = n0 + cbase + j * 32 + 16 * p;  // first column of the pair
         u32x2 d[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

@@ -70,14 +70,16 @@ def test_expert_ffn_alone(dtype, hs):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("H,h", [(256, 192), (328, 136)])
+@pytest.mark.parametrize("H,h", [(256, 192), (328, 136), (200, 120)])
 def test_expert_ffn_short_segments(dtype, H, h):
     """Segments shorter than one 256-row tile, and tails of every length class
     around the 32-row MFMA blocks and the 128-row halves of a tile: 1, 31, 32,
     33, 63, 64, 65, 96, 127, 128, 129, 160, 192, 224, 255, 257 and 300 rows.
     In a segment's last tile the kernel skips the MFMA blocks and A loads of
     rows past the segment, so every row of every segment is compared, segment
-    by segment, and the rows past the last segment must stay untouched."""
+    by segment, and the rows past the last segment must stay untouched.  Widths
+    of 120, 200 and 328 give output tiles with at most 128 valid columns, which
+    the kernel runs in its narrow wave layout."""
     sizes = [1, 31, 32, 33, 63, 64, 65, 96, 0, 127, 128, 129, 160, 192, 224, 255, 257, 300]
     E = len(sizes)
     N = sum(sizes)
