@@ -106,6 +106,8 @@ EDGE = [
     Workload("ragged", T=1000, H=200, E=6, K=2, h=136, cf=0.9),
     # shared expert, random router bias, top-4
     Workload("shared", T=512, H=128, E=8, K=4, h=64, hs=96, cf=1.25, bias="normal"),
+    # a shared expert as wide as the routed ones, with a 8-row last tile
+    Workload("shared_as_wide", T=520, H=128, E=8, K=4, h=64, hs=64, cf=1.25, bias="normal"),
     # one expert: the dense FFN
     Workload("dense", T=300, H=64, E=1, K=1, h=96),
     # the most experts and slots

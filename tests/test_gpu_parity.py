@@ -263,6 +263,9 @@ EDGE = [
     ("E256_K8", dict(T=130, H=64, E=256, K=8, h=32, cf=1.25)),
     ("E1_dense", dict(T=333, H=96, E=1, K=1, h=200, cf=0.0)),
     ("shared", dict(T=500, H=128, E=16, K=4, h=64, hs=96, cf=1.25, bias="normal")),
+    # a shared expert as wide as the routed ones (T = 700 leaves its launch a
+    # 188-row last tile)
+    ("shared_as_wide", dict(T=700, H=128, E=16, K=4, h=96, hs=96, cf=1.25, bias="normal")),
     ("E40_E_not_pow2", dict(T=700, H=256, E=40, K=3, h=264, cf=1.0, bias="normal")),
     ("E128_hot", dict(T=640, H=128, E=128, K=2, h=96, cf=0.0, bias="hot01")),
     # the bf16 router stages its weights in chunks of KC = 512 / 128 / 32 k

@@ -43,8 +43,10 @@ def relerr(got, ref):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("hs", [0, 72])
+@pytest.mark.parametrize("hs", [0, 72, 192])
 def test_expert_ffn_alone(dtype, hs):
+    """The shared expert narrower than, and (hs = 192) as wide as the routed
+    ones; T = 800 gives its launches a 32-row last tile."""
     sizes = [0, 1, 255, 256, 257, 700, 0]
     E = len(sizes)
     w = Workload("ffn_alone", T=800, H=256, E=E, K=2, h=192, hs=hs, cf=0.0, dtype=dtype)
