@@ -39,7 +39,7 @@ HIPCC_FLAGS = [
 # instructions in the K loop.  A register spill would add scratch loads and
 # stores to the count and release a wait before its stage has landed, so the
 # build refuses any scratch use or spill in them.
-NO_SCRATCH_KERNELS = ("k_grouped_gemm_bf16", "k_grouped_gemm_mx8")
+NO_SCRATCH_KERNELS = ("k_grouped_gemm_bf16", "k_grouped_gemm_w4", "k_grouped_gemm_mx8")
 
 
 def hipcc() -> str:
