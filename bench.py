@@ -549,7 +549,7 @@ def main():
                    "h_exp": w.h, "h_shared": w.hs, "capacity_factor": w.cf,
                    "kept_rows": N, "dropped_assignments": dropped,
                    "aux_loss": float(buf.aux.item())},
-        "roofline": {"kernel": "k_grouped_gemm_bf16" if w.dtype == "bf16" else "k_grouped_gemm_f32",
+        "roofline": {"kernel": "k_grouped_gemm_w4" if w.dtype == "bf16" else "k_grouped_gemm_f32",
                      "bound": "mfma", "achieved": gm["achieved"], "peak": gm["peak"],
                      "unit": "TFLOP/s", "frac": gm["frac"], "traffic": traffic,
                      "traffic_note": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, "

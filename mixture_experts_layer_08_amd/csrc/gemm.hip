@@ -448,91 +448,141 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// Row-major forward form (NN) on four waves: 256 x 256 x 32 tiles, one wave
-// per SIMD owning a 128 x 128 block as 8 x 8 v_mfma_f32_16x16x32_bf16 tiles
-// (256 fp32 accumulators per lane, in AGPRs).
+// Four-wave form: 256 x 256 x 32 tiles, one wave per SIMD owning a 128 x 128
+// block as 8 x 8 v_mfma_f32_16x16x32_bf16 tiles (256 fp32 accumulators per
+// lane, in AGPRs).  Same layouts and epilogues as the eight-wave kernel.
 //
 // Why a second kernel: the grouped GEMM is power-limited (the eight-wave
-// kernel above runs its MFMAs ~75% of its cycles at ~1.5 GHz).  With one
-// wave per SIMD and 128 x 128 per wave, a K-step reads 64 KiB of fragments
-// from LDS per CU instead of 96, and the 16 x 16 MFMA draws less power per
-// FLOP than the 32 x 32 one, so the clock holds ~1.9 GHz; the four waves
-// must then hide their own latencies, which the schedule below does.
+// kernel runs its MFMAs ~75% of its cycles at ~1.5 GHz).  With one wave per
+// SIMD and 128 x 128 per wave, a K-step reads 64 KiB of fragments from LDS
+// per CU instead of 96, and the 16 x 16 MFMA draws less power per FLOP than
+// the 32 x 32 one, so the clock holds ~1.9 GHz; the four waves must then
+// hide their own latencies, which the schedule below does.
 //
-// Stage layout and LDS-direct loads as above (4-stage ring, 32 KiB stages),
-// except the B stage's chunk swizzle: chunk c of k row k is stored at
-// c ^ (4 (k & 3) + 2 ((k >> 3) & 1)).  The fragment of k rows 8g .. 8g+7
-// that lane group g reads by transposing reads would otherwise put the rows
-// k and k + 8 of one read on the same banks.
+// Stage layout and LDS-direct loads as in the eight-wave kernel (4-stage
+// ring, 32 KiB stages), except the "cols" form's chunk swizzle: chunk c of k
+// row k is stored at c ^ (4 (k & 3) + 2 ((k >> 3) & 1)).  The fragment of k
+// rows 8g .. 8g+7 that lane group g reads by transposing reads would
+// otherwise put the rows k and k + 8 of one read on the same banks.
 //
 // Per K-step: wait until step kt+1 has landed for every wave (s_waitcnt on
 // the own loads, then the barrier, which also frees step kt-1's slot), then
 // 64 MFMAs on fragments read during the previous step, in 8 groups of 8;
 // group i also reads fragment i of both operands for step kt+1 and issues
-// refill load i.  The output layout (lane: row l % 16, columns 4 (l / 16)
-// .. +3 of each 16 x 16 tile, with the operands swapped) lets lane pairs
-// (l, l ^ 16) exchange halves and store 8 consecutive columns each.
+// refill load i.  A fragment is 8 consecutive k (k chunk l / 16) of one row
+// or column (l % 16) per lane.  With the operands swapped, lane l holds row
+// l % 16 and columns 4 (l / 16) .. +3 of each 16 x 16 output tile.
 //
-// A segment's last tile runs a predicated loop that skips the MFMAs of the
-// 16-row groups past the segment (their A rows are not fetched either).  A
-// tile with at most 128 valid columns uses 4 x 1 waves of 64 x 128 instead
-// of 2 x 2 of 128 x 128, so no wave multiplies only zeros.
+// A segment's last tile runs the loop instantiated for fewer 16-row groups
+// (their A rows are not fetched either).  A tile with at most 128 valid
+// columns (row-major forms) uses 4 x 1 waves of 64 x 128 instead of 2 x 2 of
+// 128 x 128, so no wave multiplies only zeros.
 constexpr int kW4Threads = 256;
 constexpr int kW4Dma = 4;  // LDS-direct loads per operand, per wave, per stage
-template <int EPI>
+template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
-    const bf16* __restrict__ A, const bf16* __restrict__ B, bf16* __restrict__ C,
-    bf16* __restrict__ Ep, const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows,
-    int mt_bound, int Kd, int N, int xcd_chunk) {
+    const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv, bf16* Ep,
+    const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows, int mt_bound, int M,
+    int Kd, int N, int xcd_chunk) {
+  constexpr bool kTN = LAYOUT == kGemmTN;
+  constexpr bool kARows = !kTN;               // A in "rows" form
+  constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
   int mt, nt, seg, row0, rows;
+  int k_begin = 0, k_end = Kd;  // contraction range; TN: the segment's packed rows
   {
     const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
-    if (tile >= mt_bound * nt_count) return;
-    decode_tile(tile, mt_bound, nt_count, mt, nt);
-    if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+    if (kTN) {
+      const int mt_count = (M + BM2 - 1) / BM2;
+      const int per_seg = mt_count * nt_count;
+      if (tile >= G * per_seg) return;
+      seg = tile / per_seg;
+      decode_tile(tile - seg * per_seg, mt_count, nt_count, mt, nt);
+      k_begin = offsets ? offsets[seg] : 0;
+      k_end = offsets ? offsets[seg + 1] : fixed_rows;
+      row0 = mt * BM2;  // rows of C = columns of A
+      rows = min(BM2, M - row0);
+    } else {
+      if (tile >= mt_bound * nt_count) return;
+      decode_tile(tile, mt_bound, nt_count, mt, nt);
+      if (!find_segment<BM2>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+    }
   }
   seg = __builtin_amdgcn_readfirstlane(seg);
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
+  k_begin = __builtin_amdgcn_readfirstlane(k_begin);
+  k_end = __builtin_amdgcn_readfirstlane(k_end);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n0 = nt * BN2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- global -> LDS: 4 + 4 loads per wave per stage ----
-  // A ("rows" form): load d covers stage rows 16 (4d + wave) .. +15, four
-  // lanes per 64-byte row; rows past the tile's valid rows and k past Kd read
-  // as zero.  B ("cols" form): load d covers k rows 8d + c_row0 (c_row0 =
-  // 2 wave + lane / 32), 32 lanes per 512-byte row, so (k >> 3) & 1 = d & 1;
-  // weight columns past N and k rows past Kd (beyond num_records) read as
-  // zero.
+  // "rows" form: load d covers stage rows 16 (4d + wave) .. +15, four lanes
+  // per 64-byte row; k past Kd reads as zero, and so do A rows past the
+  // tile's valid rows (not fetched).  "cols" form: load d covers k rows
+  // 8d + c_row0 (c_row0 = 2 wave + lane / 32), 32 lanes per 512-byte row, so
+  // (k >> 3) & 1 = d & 1; k rows past the contraction range lie beyond
+  // num_records, and columns past the operand's width are not fetched.
   const int r_row_l = lane >> 2;
   const int r_chunk = a_swz(r_row_l, lane & 3);
-  const u32x4 ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
-  const uint32_t a_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 8) * 2;
-  const uint32_t a_dstride = (uint32_t)(4 * 16 * Kd) * 2, a_kstride = BK2 * 2;
-  bool a_live[kW4Dma];
-#pragma unroll
-  for (int d = 0; d < kW4Dma; ++d) a_live[d] = 16 * (4 * d + wave) + r_row_l < rows;
   const int c_row0 = (lane >> 5) + 2 * wave;
   const int c_chunk0 = (lane & 31) ^ (4 * (c_row0 & 3)), c_chunk1 = c_chunk0 ^ 2;
-  const u32x4 rb_src = make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
-  const uint32_t b_off0 = (uint32_t)(c_row0 * N + c_chunk0 * 8) * 2;
-  const uint32_t b_off1 = (uint32_t)(c_row0 * N + c_chunk1 * 8) * 2;
-  const uint32_t b_dstride = (uint32_t)(8 * N) * 2, b_kstride = (uint32_t)(BK2 * N) * 2;
-  const bool b_live0 = n0 + c_chunk0 * 8 < N, b_live1 = n0 + c_chunk1 * 8 < N;
+  // A
+  u32x4 ra_src;
+  uint32_t a_off0, a_off1, a_dstride, a_kstride;
+  bool a_live[kW4Dma];
+  if (kARows) {
+    ra_src = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd * 2);
+    a_off0 = a_off1 = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 8) * 2;
+    a_dstride = (uint32_t)(4 * 16 * Kd) * 2;
+    a_kstride = BK2 * 2;
+#pragma unroll
+    for (int d = 0; d < kW4Dma; ++d) a_live[d] = 16 * (4 * d + wave) + r_row_l < rows;
+  } else {
+    // TN: A_g^T; k rows are the segment's packed rows, columns row0.. of A
+    ra_src = make_rsrc_words(A + (size_t)k_begin * M + row0,
+                             ((long long)(k_end - k_begin) * M - row0) * 2);
+    a_off0 = (uint32_t)(c_row0 * M + c_chunk0 * 8) * 2;
+    a_off1 = (uint32_t)(c_row0 * M + c_chunk1 * 8) * 2;
+    a_dstride = (uint32_t)(8 * M) * 2;
+    a_kstride = (uint32_t)(BK2 * M) * 2;
+#pragma unroll
+    for (int d = 0; d < kW4Dma; ++d) a_live[d] = row0 + ((d & 1) ? c_chunk1 : c_chunk0) * 8 < M;
+  }
+  // B
+  u32x4 rb_src;
+  uint32_t b_off0, b_off1, b_dstride, b_kstride;
+  bool b_live0 = true, b_live1 = true;
+  if (kBRows) {
+    // NT: B_g^T rows n0.. (rows past N lie beyond num_records)
+    rb_src = make_rsrc_words(B + ((size_t)seg * N + n0) * Kd, (long long)(N - n0) * Kd * 2);
+    b_off0 = b_off1 = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 8) * 2;
+    b_dstride = (uint32_t)(4 * 16 * Kd) * 2;
+    b_kstride = BK2 * 2;
+  } else {
+    rb_src = kTN ? make_rsrc_words(B + (size_t)k_begin * N + n0,
+                                   ((long long)(k_end - k_begin) * N - n0) * 2)
+                 : make_rsrc_words(B + (size_t)seg * Kd * N + n0, ((long long)Kd * N - n0) * 2);
+    b_off0 = (uint32_t)(c_row0 * N + c_chunk0 * 8) * 2;
+    b_off1 = (uint32_t)(c_row0 * N + c_chunk1 * 8) * 2;
+    b_dstride = (uint32_t)(8 * N) * 2;
+    b_kstride = (uint32_t)(BK2 * N) * 2;
+    b_live0 = n0 + c_chunk0 * 8 < N;
+    b_live1 = n0 + c_chunk1 * 8 < N;
+  }
   auto dma = [&](uint32_t st, int d, int kt) {
     if (d < kW4Dma) {
-      const uint32_t off = a_off + d * a_dstride + (uint32_t)kt * a_kstride;
-      dma_load16(st + (4 * d + wave) * 1024,
-                 kt * BK2 + r_chunk * 8 < Kd && a_live[d] ? off : kOob, ra_src);
+      const uint32_t off = ((d & 1) ? a_off1 : a_off0) + d * a_dstride + (uint32_t)kt * a_kstride;
+      const bool ok = kARows ? kt * BK2 + r_chunk * 8 < Kd && a_live[d] : a_live[d];
+      dma_load16(st + (4 * d + wave) * 1024, ok ? off : kOob, ra_src);
     } else {
       const int e = d - kW4Dma;
       const uint32_t off = ((e & 1) ? b_off1 : b_off0) + e * b_dstride + (uint32_t)kt * b_kstride;
-      dma_load16(st + BM2 * BK2 * 2 + (4 * e + wave) * 1024,
-                 ((e & 1) ? b_live1 : b_live0) ? off : kOob, rb_src);
+      const bool ok = kBRows ? kt * BK2 + r_chunk * 8 < Kd : ((e & 1) ? b_live1 : b_live0);
+      dma_load16(st + BM2 * BK2 * 2 + (4 * e + wave) * 1024, ok ? off : kOob, rb_src);
     }
   };
   auto stage_addr = [&](int kt) {
@@ -540,19 +590,29 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   };
 
   // ---- wave block and fragment addresses ----
-  const bool narrow = N - n0 <= BN2 / 2;
+  const bool narrow = !kTN && N - n0 <= BN2 / 2;
   const int rbase = narrow ? wave * 64 : (wave >> 1) * 128;
   const int cbase = narrow ? 0 : (wave & 1) * 128;
   const int li = lane & 15, lg = lane >> 4;
-  // A fragment i: row rbase + 16 i + li, k chunk lg (one b128 read)
-  const uint32_t a_rd = (uint32_t)(rbase + li) * 64 + 16 * (lg ^ ((li >> 2) & 3));
-  // B fragment j: columns cbase + 16 j + 4 (li % 4) .. +3 of k rows 8 lg +
-  // li / 4 and, +2048 bytes, 4 rows further (two transposing reads give lane
-  // column li, k 8 lg .. +7).  With the swizzle above, the 32-byte column
-  // step j becomes an XOR with 32 (j ^ (2 (li / 4) + lg % 2)).
-  const uint32_t b_rd = BM2 * BK2 * 2 + (uint32_t)(8 * lg + (li >> 2)) * 512 +
-                        16 * (cbase / 8 + ((li >> 1) & 1)) + 8 * (li & 1) +
-                        32 * (2 * (li >> 2) + (lg & 1));
+  // "rows" fragment f of a block starting at row r0: row r0 + 16 f + li, k
+  // chunk lg (one b128 read at +1024 f).  "cols" fragment f of a block
+  // starting at column c0 (a multiple of 128): columns c0 + 16 f + 4 (li %
+  // 4) .. +3 of k rows 8 lg + li / 4 and, +2048 bytes, 4 rows further (two
+  // transposing reads give lane column li, k 8 lg .. +7); with the swizzle,
+  // the 32-byte column step f becomes an XOR with 32 (f ^ (2 (li / 4) +
+  // lg % 2)).
+  auto rows_rd = [&](int r0) { return (uint32_t)(r0 + li) * 64 + 16 * (lg ^ ((li >> 2) & 3)); };
+  auto cols_rd = [&](int c0) {
+    return (uint32_t)(8 * lg + (li >> 2)) * 512 + 16 * (c0 / 8 + ((li >> 1) & 1)) + 8 * (li & 1) +
+           32 * (2 * (li >> 2) + (lg & 1));
+  };
+  const uint32_t a_rd = kARows ? rows_rd(rbase) : cols_rd(rbase);
+  const uint32_t b_rd = BM2 * BK2 * 2 + (kBRows ? rows_rd(cbase) : cols_rd(cbase));
+  auto frag = [&](bool rows_form, uint32_t st, uint32_t rd, int f) {
+    if (rows_form) return lds_read_b128(st + rd + f * 1024);
+    const uint32_t ad = st + (rd ^ (32u * f));
+    return lds_read_tr_pair(ad, ad + 2048);
+  };
   // 16-row groups of the block that hold rows (8 = all, the common case),
   // rounded up to a pair: the loop is instantiated for 0, 2, 4, 6, 8
   const int ng = __builtin_amdgcn_readfirstlane(
@@ -565,15 +625,6 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
                                                           0, 0, 0);
     else
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  };
-  auto read_frags = [&](uint32_t st, bf16x8* a, bf16x8* b) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = lds_read_b128(st + a_rd + i * 1024);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t ad = st + (b_rd ^ (32u * j));
-      b[j] = lds_read_tr_pair(ad, ad + 2048);
-    }
   };
   // One K-step with the MFMAs of the first NG groups.  The first step's
   // accumulators start from a zero C operand, so that the compiler never
@@ -595,9 +646,8 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      na[i] = lds_read_b128(st1 + a_rd + i * 1024);
-      const uint32_t ad = st1 + (b_rd ^ (32u * i));
-      nb[i] = lds_read_tr_pair(ad, ad + 2048);
+      na[i] = frag(kARows, st1, a_rd, i);
+      nb[i] = frag(kBRows, st1, b_rd, i);
       dma(stf, i, kt + kStages - 1);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
@@ -609,7 +659,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   };
   using kTrue = std::integral_constant<bool, true>;
   using kFalse = std::integral_constant<bool, false>;
-  const int KT = (Kd + BK2 - 1) / BK2;
+  const int KT = (k_end - k_begin + BK2 - 1) / BK2;
   // These vmcnt counts hold only while the LDS-direct loads are the loop's
   // only vector-memory instructions: the build refuses a spill.
 #pragma unroll
@@ -622,7 +672,11 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   block_barrier();                             // ... and every wave's
   auto k_loop = [&](auto ng_c) {
     bf16x8 pa[8], pb[8], qa[8], qb[8];
-    read_frags(lds0, pa, pb);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      pa[f] = frag(kARows, lds0, a_rd, f);
+      pb[f] = frag(kBRows, lds0, b_rd, f);
+    }
     step(ng_c, kTrue{}, 0, pa, pb, qa, qb);
     int kt = 1;
     for (; kt + 1 < KT; kt += 2) {
@@ -640,9 +694,13 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 
   // ---- epilogue: lane holds row rbase + 16 i + li, columns cbase + 16 j +
-  // 4 lg .. +3.  For each pair of tiles (2p, 2p + 1), even lg stores columns
-  // 16 (2p) + 4 lg .. +7 (its own 4 and its partner's), odd lg columns
-  // 16 (2p + 1) + 4 (lg - 1) .. +7.
+  // 4 lg .. +3.  The weight-gradient form stores its fp32 groups of 4
+  // directly.  The bf16 forms pair tiles (2p, 2p + 1): even lg stores
+  // columns 16 (2p) + 4 lg .. +7 (its own 4 and its partner's, lane l ^ 16),
+  // odd lg columns 16 (2p + 1) + 4 (lg - 1) .. +7.  Each lane reads what it
+  // needs of Ep / C (GELU', accumulate) for its own 4 columns before the
+  // exchange, so an in-place epilogue reads every element before it is
+  // written.
   // The lane's coordinates are recomputed here from a fresh lane id (an
   // instruction the compiler cannot hoist): kept live across the K loop they
   // would not fit beside its fragments and spill, and a spill's scratch
@@ -657,6 +715,16 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   for (int i = 0; i < 8; ++i) {
     const int m = rbase_e + 16 * i + li_e;
     if (i >= ng || m >= rows) continue;  // uniform over the lane pair (l, l ^ 16)
+    if (kTN) {
+      float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = n0 + cbase_e + 16 * j + 4 * lg_e;
+        if (c < N) *(f32x4*)(crow + c) = acc[i][j];
+      }
+      continue;
+    }
+    bf16* crow = (bf16*)Cv + (size_t)(row0 + m) * N;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       u32x2 d[2];
@@ -665,13 +733,27 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
         const int j = 2 * p + h;
         float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
         const int c = n0 + cbase_e + 16 * j + 4 * lg_e;  // this lane's 4 columns
-        if (EPI == kEpiGeluSave && c < N)
-          *(u32x2*)(Ep + (size_t)(row0 + m) * N + c) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        const bool ok = c < N;                           // whole group of 4 in or out
+        const size_t at = (size_t)(row0 + m) * N + c;
+        if (EPI == kEpiGeluSave && ok)
+          *(u32x2*)(Ep + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         if (EPI == kEpiGelu || EPI == kEpiGeluSave) {
           v0 = gelu_tanh_f32(v0);
           v1 = gelu_tanh_f32(v1);
           v2 = gelu_tanh_f32(v2);
           v3 = gelu_tanh_f32(v3);
+        } else if (EPI == kEpiGeluGrad) {
+          const u32x2 u = ok ? *(const u32x2*)(Ep + at) : u32x2{0u, 0u};
+          v0 *= gelu_tanh_grad_f32(bf16_lo(u[0]));
+          v1 *= gelu_tanh_grad_f32(bf16_hi(u[0]));
+          v2 *= gelu_tanh_grad_f32(bf16_lo(u[1]));
+          v3 *= gelu_tanh_grad_f32(bf16_hi(u[1]));
+        } else if (EPI == kEpiAccum) {
+          const u32x2 cc = ok ? *(const u32x2*)(crow + c) : u32x2{0u, 0u};
+          v0 += bf16_lo(cc[0]);
+          v1 += bf16_hi(cc[0]);
+          v2 += bf16_lo(cc[1]);
+          v3 += bf16_hi(cc[1]);
         }
         d[h] = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
@@ -680,7 +762,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
       const uint32_t x1 = (uint32_t)__shfl_xor((int)send[1], 16, kWave);
       const u32x4 o = odd ? u32x4{x0, x1, d[1][0], d[1][1]} : u32x4{d[0][0], d[0][1], x0, x1};
       const int c0 = n0 + cbase_e + 16 * (2 * p + (odd ? 1 : 0)) + 4 * (lg_e & ~1);
-      if (c0 < N) *(u32x4*)(C + (size_t)(row0 + m) * N + c0) = o;
+      if (c0 < N) *(u32x4*)(crow + c0) = o;
     }
   }
 }
@@ -781,6 +863,14 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
   return (a.max_rows + tm - 1) / tm + a.G;
 }
 
+// Layouts that run on the four-wave kernel (the others, and contractions of
+// at most two K-steps, on the eight-wave one).
+#ifndef MOE_W4_LAYOUTS
+#define MOE_W4_LAYOUTS 7  // bit per layout: NN 1, NT 2, TN 4
+#endif
+template <int LAYOUT>
+constexpr bool kUseW4 = ((MOE_W4_LAYOUTS >> LAYOUT) & 1) != 0;
+
 template <int LAYOUT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
   const hipError_t e = allow_dynamic_lds<k_grouped_gemm_bf16<LAYOUT, EPI>, true>();
@@ -796,13 +886,14 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
   }
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if constexpr (LAYOUT == kGemmNN &&
-                (EPI == kEpiStore || EPI == kEpiGelu || EPI == kEpiGeluSave)) {
-    const hipError_t e4 = allow_dynamic_lds<k_grouped_gemm_w4<EPI>, true>();
+  // A contraction of one or two K-steps (the d_logits W_r^T accumulate: E
+  // rounded up to 8) is all epilogue, which eight waves share better.
+  if (kUseW4<LAYOUT> && (LAYOUT == kGemmTN || a.Kd > 2 * BK2)) {
+    const hipError_t e4 = allow_dynamic_lds<k_grouped_gemm_w4<LAYOUT, EPI>, true>();
     if (e4 != hipSuccess) return e4;
-    k_grouped_gemm_w4<EPI><<<(unsigned)grid, kW4Threads, kSmem2, st>>>(
-        (const bf16*)a.A, (const bf16*)a.B, (bf16*)a.C, (bf16*)a.E, a.offsets, a.G,
-        a.fixed_rows, a.offsets ? a.max_rows : a.fixed_rows, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
+    k_grouped_gemm_w4<LAYOUT, EPI><<<(unsigned)grid, kW4Threads, kSmem2, st>>>(
+        (const bf16*)a.A, (const bf16*)a.B, a.C, (bf16*)a.E, a.offsets, a.G, a.fixed_rows,
+        a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N, xcd_chunk_for(ntc));
     return hipGetLastError();
   }
   k_grouped_gemm_bf16<LAYOUT, EPI><<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(

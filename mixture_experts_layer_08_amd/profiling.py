@@ -35,10 +35,11 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # Kernel families: the dispatches summarised and the sources their hash covers.
-#   bf16: the forward's row-major (NN) instantiations, GEMM1 with GELU and GEMM2
+#   bf16: the forward's row-major (NN) instantiations of the four-wave kernel,
+#         GEMM1 with GELU and GEMM2
 #   mx8:  the MXFP8 grouped GEMM (both epilogues)
 KERNELS = {
-    "bf16": (re.compile(r"k_grouped_gemm_bf16<\s*0\s*,"), ("gemm.hip", "gemm_common.h")),
+    "bf16": (re.compile(r"k_grouped_gemm_w4<\s*0\s*,"), ("gemm.hip", "gemm_common.h")),
     "mx8": (re.compile(r"k_grouped_gemm_mx8<"), ("gemm_mx8.hip", "gemm_common.h", "mx.h")),
 }
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
@@ -164,8 +165,8 @@ def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz:
       - MFMA busy per cycle = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / (effective
         clock x duration), and of the peak clock.  Their product is the
         fraction of dense MFMA peak."""
-    pats = {"k_grouped_gemm_bf16 (GEMM1, GELU)": r"k_grouped_gemm_bf16<\s*0\s*,\s*1>",
-            "k_grouped_gemm_bf16 (GEMM2)": r"k_grouped_gemm_bf16<\s*0\s*,\s*0>",
+    pats = {"k_grouped_gemm_w4 (GEMM1, GELU)": r"k_grouped_gemm_w4<\s*0\s*,\s*1>",
+            "k_grouped_gemm_w4 (GEMM2)": r"k_grouped_gemm_w4<\s*0\s*,\s*0>",
             "k_grouped_gemm_mx8 (GEMM1, GELU)": r"k_grouped_gemm_mx8<1>",
             "k_grouped_gemm_mx8 (GEMM2)": r"k_grouped_gemm_mx8<0>",
             "k_permute (memory-bound)": r"k_permute<",
