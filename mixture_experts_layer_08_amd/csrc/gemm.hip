@@ -383,6 +383,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // columns: lane kh = 0 stores columns 16 p .. 16 p + 7, kh = 1 columns
   // 16 p + 8 .. 16 p + 15, one 16-byte store each (the weight-gradient form
   // stores its fp32 groups of 4 directly).
+  // GELU' and accumulate read a bf16 tensor that may be C itself: every
+  // value this lane needs is loaded before the first store (one memory
+  // latency per tile, not one per store the loads could not pass).
+  constexpr bool kReads = EPI == kEpiGeluGrad || EPI == kEpiAccum;
+  u32x2 rd[kReads ? 4 : 1][kReads ? 2 : 1][kReads ? 4 : 1];
+  if (kReads) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = rbase + i * 32 + rr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = n0 + cbase + j * 32 + 8 * g + 4 * kh;
+          const bf16* src = EPI == kEpiGeluGrad ? Ep : (const bf16*)Cv;
+          rd[kReads ? i : 0][kReads ? j : 0][kReads ? g : 0] =
+              i < na_max && m < rows && c < N ? *(const u32x2*)(src + (size_t)(row0 + m) * N + c)
+                                              : u32x2{0u, 0u};
+        }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = rbase + i * 32 + rr;
@@ -421,13 +442,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
             v2 = gelu_tanh_f32(v2);
             v3 = gelu_tanh_f32(v3);
           } else if (EPI == kEpiGeluGrad) {
-            const u32x2 u = ok ? *(const u32x2*)(Ep + at) : u32x2{0u, 0u};
+            const u32x2 u = rd[kReads ? i : 0][kReads ? j : 0][kReads ? g : 0];
             v0 *= gelu_tanh_grad_f32(bf16_lo(u[0]));
             v1 *= gelu_tanh_grad_f32(bf16_hi(u[0]));
             v2 *= gelu_tanh_grad_f32(bf16_lo(u[1]));
             v3 *= gelu_tanh_grad_f32(bf16_hi(u[1]));
           } else if (EPI == kEpiAccum) {
-            const u32x2 c = ok ? *(const u32x2*)(crow + at) : u32x2{0u, 0u};
+            const u32x2 c = rd[kReads ? i : 0][kReads ? j : 0][kReads ? g : 0];
             v0 += bf16_lo(c[0]);
             v1 += bf16_hi(c[0]);
             v2 += bf16_lo(c[1]);
@@ -711,6 +732,25 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   const bool odd = lg_e & 1;
   const int rbase_e = narrow ? wave * 64 : (wave >> 1) * 128;
   const int cbase_e = narrow ? 0 : (wave & 1) * 128;
+  // GELU' and accumulate read a bf16 tensor that may be C itself: every
+  // value this lane needs is loaded before the first store (one memory
+  // latency per tile, not one per store the loads could not pass).
+  constexpr bool kReads = EPI == kEpiGeluGrad || EPI == kEpiAccum;
+  u32x2 rd[kReads ? 8 : 1][kReads ? 8 : 1];
+  if (kReads) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = rbase_e + 16 * i + li_e;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = n0 + cbase_e + 16 * j + 4 * lg_e;
+        const bf16* src = EPI == kEpiGeluGrad ? Ep : (const bf16*)Cv;
+        rd[kReads ? i : 0][kReads ? j : 0] =
+            i < ng && m < rows && c < N ? *(const u32x2*)(src + (size_t)(row0 + m) * N + c)
+                                        : u32x2{0u, 0u};
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int m = rbase_e + 16 * i + li_e;
@@ -743,13 +783,13 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
           v2 = gelu_tanh_f32(v2);
           v3 = gelu_tanh_f32(v3);
         } else if (EPI == kEpiGeluGrad) {
-          const u32x2 u = ok ? *(const u32x2*)(Ep + at) : u32x2{0u, 0u};
+          const u32x2 u = rd[kReads ? i : 0][kReads ? j : 0];
           v0 *= gelu_tanh_grad_f32(bf16_lo(u[0]));
           v1 *= gelu_tanh_grad_f32(bf16_hi(u[0]));
           v2 *= gelu_tanh_grad_f32(bf16_lo(u[1]));
           v3 *= gelu_tanh_grad_f32(bf16_hi(u[1]));
         } else if (EPI == kEpiAccum) {
-          const u32x2 cc = ok ? *(const u32x2*)(crow + c) : u32x2{0u, 0u};
+          const u32x2 cc = rd[kReads ? i : 0][kReads ? j : 0];
           v0 += bf16_lo(cc[0]);
           v1 += bf16_hi(cc[0]);
           v2 += bf16_lo(cc[1]);
