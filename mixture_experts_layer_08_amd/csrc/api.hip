@@ -34,7 +34,7 @@ int64_t capacity_of(const moe_shape* s) {
 }
 
 struct WsLayout {
-  size_t hist, psum, base, lrank, cnt, seg;
+  size_t hist, psum, base, lrank, cnt, seg, pe;
   // MOE_FLAG_TRAIN only: GELU pre-activations (routed, shared), the router
   // weight gradient's partials, and bf16 copies of d_logits / W_r padded to
   // a multiple of 8 experts for the d_logits * W_r^T GEMM
@@ -63,6 +63,8 @@ WsLayout ws_layout(const moe_shape* s) {
   off += align_up((size_t)s->E * 4);
   L.seg = off;
   off += align_up((size_t)(2 * s->E + 2) * 4);
+  L.pe = off;  // per-expert probability totals (doubles) between the aux kernels
+  off += align_up((size_t)s->E * 8);
   if (s->flags & MOE_FLAG_TRAIN) {
     const size_t elem = s->dtype == MOE_BF16 ? 2 : 4;
     const size_t nch = (size_t)route_bwd_chunks(s->T, s->E);
@@ -296,8 +298,8 @@ moe_status moe_aux_loss(const moe_shape* s, const void* ws, size_t ws_bytes, flo
   void* w = const_cast<void*>(ws);
   return hip_status(launch_aux(at<int32_t>(w, L.hist), at<float>(w, L.psum), aux,
                                at<int32_t>(w, L.base), at<int32_t>(w, L.cnt),
-                               at<int32_t>(w, L.seg), s->T, s->E, s->K, (int)capacity_of(s),
-                               n_route_blocks(s), (hipStream_t)stream));
+                               at<double>(w, L.pe), at<int32_t>(w, L.seg), s->T, s->E, s->K,
+                               (int)capacity_of(s), n_route_blocks(s), (hipStream_t)stream));
 }
 
 moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* topk_ids, void* ws,

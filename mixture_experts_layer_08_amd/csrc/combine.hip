@@ -163,87 +163,71 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-__global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__ hist,
-                                                     const float* __restrict__ psum,
-                                                     float* __restrict__ aux,
-                                                     int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ cnt_out,
-                                                     int32_t* __restrict__ seg, int T, int E,
-                                                     int K, int C, int nblk) {
-  __shared__ double s_p[256];
-  __shared__ int s_cnt[256];
-  constexpr int kPer = 8;    // blocks per lane per chunk
-  constexpr int kBatch = 2;  // experts whose loads are in flight together
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = kAuxThreads / kWave;
-  for (int e0 = wave; e0 < E; e0 += nwaves * kBatch) {
-    int carry[kBatch];
-    double P[kBatch];
+// Block scan of expert e's per-block histogram (the block bases) and its
+// totals: the count and the sum of its per-block probability sums, in a fixed
+// order.  One wave; kPer slices of 64 blocks in flight per lane.
+__device__ __forceinline__ void aux_expert(const int32_t* __restrict__ hist,
+                                           const float* __restrict__ psum,
+                                           int32_t* __restrict__ base, int e, int nblk, int lane,
+                                           int& count, double& p_sum) {
+  constexpr int kPer = 8;
+  int carry = 0;
+  double P = 0.0;
+  const int32_t* h = hist + (size_t)e * nblk;
+  const float* ps = psum + (size_t)e * nblk;
+  int32_t* bo = base + (size_t)e * nblk;
+  for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
+    int v[kPer];
+    float pv[kPer];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      carry[j] = 0;
-      P[j] = 0.0;
+    for (int i = 0; i < kPer; ++i) {
+      const int b = b0 + 64 * i + lane;
+      v[i] = b < nblk ? h[b] : 0;
+      pv[i] = b < nblk ? ps[b] : 0.0f;
     }
-    for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
-      int v[kBatch][kPer];
-      float pv[kBatch][kPer];
+    // the kPer wave scans are independent (their DPP steps overlap); the
+    // carries from slice to slice are added afterwards
+    int incl[kPer];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = e0 + j * nwaves;
+    for (int i = 0; i < kPer; ++i) incl[i] = wave_scan_dpp(v[i]);
+    double part = 0.0;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int b = b0 + 64 * i + lane;
-          const bool ok = e < E && b < nblk;
-          v[j][i] = ok ? hist[(size_t)e * nblk + b] : 0;
-          pv[j][i] = ok ? psum[(size_t)e * nblk + b] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = e0 + j * nwaves;
-        if (e >= E) break;  // wave-uniform
-        double ps = 0.0;
-        int32_t* bo = base + (size_t)e * nblk;
-        // the 8 wave scans are independent (their shuffles overlap); the
-        // carries from row to row are added afterwards
-        int incl[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) incl[i] = wave_scan_dpp(v[j][i]);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          ps += (double)pv[j][i];
-          const int b = b0 + 64 * i + lane;
-          if (b < nblk) bo[b] = carry[j] + incl[i] - v[j][i];
-          carry[j] += __builtin_amdgcn_readlane(incl[i], 63);
-        }
-        P[j] += wave_sum_f64(ps);
-      }
+    for (int i = 0; i < kPer; ++i) {
+      part += (double)pv[i];
+      const int b = b0 + 64 * i + lane;
+      if (b < nblk) bo[b] = carry + incl[i] - v[i];
+      carry += __builtin_amdgcn_readlane(incl[i], 63);
     }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int e = e0 + j * nwaves;
-        if (e < E) {
-          cnt_out[e] = carry[j];
-          s_cnt[e] = carry[j];
-          s_p[e] = P[j];
-        }
-      }
-    }
+    P += wave_sum_f64(part);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int e = 0; e < E; ++e) s += ((double)s_cnt[e] / ((double)T * K)) * (s_p[e] / (double)T);
-    *aux = (float)((double)E * s);
+  count = carry;
+  p_sum = P;
+}
+
+// aux = E sum_e (count_e / (T K)) (P_e / T), by one wave: lane l adds
+// experts 4l .. 4l+3 in order, then a fixed shuffle tree (deterministic).
+// The segments from the counts, by another wave (E <= 256: lane l holds
+// experts 4l .. 4l+3).
+__device__ __forceinline__ void aux_finish(const int* cnt, const double* p, float* __restrict__ aux,
+                                           int32_t* __restrict__ seg, int T, int E, int K, int C,
+                                           int wave, int lane) {
+  if (wave == 1) {
+    const double inv_tk = 1.0 / ((double)T * K), inv_t = 1.0 / (double)T;
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) part += ((double)cnt[e] * inv_tk) * (p[e] * inv_t);
+    }
+    const double s = wave_sum_f64(part);
+    if (lane == 0) *aux = (float)((double)E * s);
   }
   if (wave == 0) {
-    // segments from the counts (E <= 256: lane l holds experts 4l .. 4l+3)
     int kept4[4], run = 0, drop = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      const int c = e < E ? s_cnt[e] : 0;
+      const int c = e < E ? cnt[e] : 0;
       kept4[i] = min(c, C);
       drop += c - kept4[i];
       run += kept4[i];
@@ -265,10 +249,71 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__
   }
 }
 
+// Up to kAuxWaves experts: one workgroup, one wave per expert, then the aux
+// loss and the segments from LDS.
+constexpr int kAuxWaves = kAuxThreads / kWave;
+__global__ __launch_bounds__(kAuxThreads) void k_aux(const int32_t* __restrict__ hist,
+                                                     const float* __restrict__ psum,
+                                                     float* __restrict__ aux,
+                                                     int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ cnt_out,
+                                                     int32_t* __restrict__ seg, int T, int E,
+                                                     int K, int C, int nblk) {
+  __shared__ double s_p[kAuxWaves];
+  __shared__ int s_cnt[kAuxWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave < E) {
+    int c;
+    double P;
+    aux_expert(hist, psum, base, wave, nblk, lane, c, P);
+    if (lane == 0) {
+      cnt_out[wave] = c;
+      s_cnt[wave] = c;
+      s_p[wave] = P;
+    }
+  }
+  __syncthreads();
+  aux_finish(s_cnt, s_p, aux, seg, T, E, K, C, wave, lane);
+}
+
+// More experts: kAuxWaves per workgroup, one wave each, totals to global ...
+__global__ __launch_bounds__(kAuxThreads) void k_aux_scan(const int32_t* __restrict__ hist,
+                                                          const float* __restrict__ psum,
+                                                          int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ cnt_out,
+                                                          double* __restrict__ p_out, int E,
+                                                          int nblk) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kAuxWaves + (threadIdx.x >> 6);
+  if (e >= E) return;  // wave-uniform; no barrier in this kernel
+  int c;
+  double P;
+  aux_expert(hist, psum, base, e, nblk, lane, c, P);
+  if (lane == 0) {
+    cnt_out[e] = c;
+    p_out[e] = P;
+  }
+}
+
+// ... and one small workgroup for the aux loss and the segments.
+__global__ __launch_bounds__(128) void k_aux_finish(const int32_t* __restrict__ cnt,
+                                                    const double* __restrict__ p,
+                                                    float* __restrict__ aux,
+                                                    int32_t* __restrict__ seg, int T, int E, int K,
+                                                    int C) {
+  aux_finish(cnt, p, aux, seg, T, E, K, C, threadIdx.x >> 6, threadIdx.x & 63);
+}
+
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int32_t* base,
-                      int32_t* cnt, int32_t* seg, int T, int E, int K, int C, int nblk,
-                      hipStream_t st) {
-  k_aux<<<1, kAuxThreads, 0, st>>>(hist, psum, aux, base, cnt, seg, T, E, K, C, nblk);
+                      int32_t* cnt, double* p_scratch, int32_t* seg, int T, int E, int K, int C,
+                      int nblk, hipStream_t st) {
+  if (E <= kAuxWaves) {
+    k_aux<<<1, kAuxThreads, 0, st>>>(hist, psum, aux, base, cnt, seg, T, E, K, C, nblk);
+    return hipGetLastError();
+  }
+  k_aux_scan<<<(E + kAuxWaves - 1) / kAuxWaves, kAuxThreads, 0, st>>>(hist, psum, base, cnt,
+                                                                       p_scratch, E, nblk);
+  k_aux_finish<<<1, 128, 0, st>>>(cnt, p_scratch, aux, seg, T, E, K, C);
   return hipGetLastError();
 }
 

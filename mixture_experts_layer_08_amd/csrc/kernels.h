@@ -179,14 +179,17 @@ hipError_t launch_combine_mx8(const CombineMx8Args& a, hipStream_t st);
 hipError_t launch_quantize_weight_mx8(const void* w, bool bf16_in, int G, int Kd, int N,
                                       uint8_t* q, uint8_t* s, hipStream_t st);
 
-// The aux loss from the router's per-block partials, and in the same
-// workgroup the permutation's block scan: base [E][nblk] = per-expert
-// exclusive prefix over route blocks of the block histograms, cnt [E] = the
-// per-expert totals, seg [2E + 2] = segment offsets (E + 1), kept (E) and
-// the number of dropped assignments at capacity C.
+// The aux loss from the router's per-block partials, and with it the
+// permutation's block scan: base [E][nblk] = per-expert exclusive prefix over
+// route blocks of the block histograms, cnt [E] = the per-expert totals, seg
+// [2E + 2] = segment offsets (E + 1), kept (E) and the number of dropped
+// assignments at capacity C.  Up to 16 experts one workgroup does it all;
+// more experts are scanned by one wave each over several workgroups, which
+// leave their probability totals in p_scratch [E] (doubles) for a second,
+// one-workgroup kernel.
 hipError_t launch_aux(const int32_t* hist, const float* psum, float* aux, int32_t* base,
-                      int32_t* cnt, int32_t* seg, int T, int E, int K, int C, int nblk,
-                      hipStream_t st);
+                      int32_t* cnt, double* p_scratch, int32_t* seg, int T, int E, int K, int C,
+                      int nblk, hipStream_t st);
 
 // ---- backward ----
 struct CombineBwdArgs {
