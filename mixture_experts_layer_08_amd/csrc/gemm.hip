@@ -611,12 +611,21 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   };
 
   // ---- wave block and fragment addresses ----
+  // Row-major forms: the 16 row groups of the tile are dealt to the two waves
+  // of a column half in turn (group g to row-wave g % 2), so that a segment's
+  // last tile, whose valid rows are a prefix, gives every SIMD (one wave
+  // each) about the same number of groups to multiply.  The narrow layout
+  // (four waves of 64 contiguous rows) and the weight-gradient form (A in
+  // "cols" form, contiguous 128-row blocks) keep contiguous groups.
   const bool narrow = !kTN && N - n0 <= BN2 / 2;
-  const int rbase = narrow ? wave * 64 : (wave >> 1) * 128;
+  const bool inter = !kTN && !narrow;
+  const int r0 = kTN ? (wave >> 1) * 128 : (narrow ? wave * 64 : 16 * (wave >> 1));
+  const int rstep = inter ? 32 : 16;  // rows between a wave's groups
   const int cbase = narrow ? 0 : (wave & 1) * 128;
   const int li = lane & 15, lg = lane >> 4;
-  // "rows" fragment f of a block starting at row r0: row r0 + 16 f + li, k
-  // chunk lg (one b128 read at +1024 f).  "cols" fragment f of a block
+  // "rows" fragment f: row r + f * step + li of the rows r, r + step, ...
+  // (step 16 for the weight operand, rstep for A), k chunk lg (one b128 read
+  // at + 64 step f).  "cols" fragment f of a block
   // starting at column c0 (a multiple of 128): columns c0 + 16 f + 4 (li %
   // 4) .. +3 of k rows 8 lg + li / 4 and, +2048 bytes, 4 rows further (two
   // transposing reads give lane column li, k 8 lg .. +7); with the swizzle,
@@ -627,17 +636,17 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     return (uint32_t)(8 * lg + (li >> 2)) * 512 + 16 * (c0 / 8 + ((li >> 1) & 1)) + 8 * (li & 1) +
            32 * (2 * (li >> 2) + (lg & 1));
   };
-  const uint32_t a_rd = kARows ? rows_rd(rbase) : cols_rd(rbase);
+  const uint32_t a_rd = kARows ? rows_rd(r0) : cols_rd(r0);
   const uint32_t b_rd = BM2 * BK2 * 2 + (kBRows ? rows_rd(cbase) : cols_rd(cbase));
-  auto frag = [&](bool rows_form, uint32_t st, uint32_t rd, int f) {
-    if (rows_form) return lds_read_b128(st + rd + f * 1024);
+  auto frag = [&](bool rows_form, uint32_t st, uint32_t rd, uint32_t fstride, int f) {
+    if (rows_form) return lds_read_b128(st + rd + f * fstride);
     const uint32_t ad = st + (rd ^ (32u * f));
     return lds_read_tr_pair(ad, ad + 2048);
   };
-  // 16-row groups of the block that hold rows (8 = all, the common case),
-  // rounded up to a pair: the loop is instantiated for 0, 2, 4, 6, 8
+  // this wave's row groups that hold rows (8 = all, the common case), rounded
+  // up to a pair: the loop is instantiated for 0, 2, 4, 6, 8
   const int ng = __builtin_amdgcn_readfirstlane(
-      min(max(((rows - rbase + 31) >> 5) * 2, 0), narrow ? 4 : 8));
+      min(max((((rows - r0 + rstep - 1) >> (inter ? 5 : 4)) + 1) & ~1, 0), narrow ? 4 : 8));
 
   f32x4 acc[8][8];  // set by the first step's MFMAs (zero C operand)
   auto mma = [&](auto first_c, int i, int j, const bf16x8* a, const bf16x8* b) {
@@ -650,9 +659,10 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // One K-step with the MFMAs of the first NG groups.  The first step's
   // accumulators start from a zero C operand, so that the compiler never
   // materialises 256 zeros in ordinary registers.
-  auto step = [&](auto ng_c, auto first_c, int kt, const bf16x8* ca, const bf16x8* cb,
-                  bf16x8* na, bf16x8* nb) {
+  auto step = [&](auto ng_c, auto first_c, auto afs_c, int kt, const bf16x8* ca,
+                  const bf16x8* cb, bf16x8* na, bf16x8* nb) {
     constexpr int NG = decltype(ng_c)::value;
+    constexpr uint32_t AFS = decltype(afs_c)::value;  // A fragment stride (rows form)
     wait_vmcnt<(kStages - 3) * 2 * kW4Dma>();
     block_barrier();
     const uint32_t st1 = stage_addr(kt + 1);
@@ -667,8 +677,8 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      na[i] = frag(kARows, st1, a_rd, i);
-      nb[i] = frag(kBRows, st1, b_rd, i);
+      na[i] = frag(kARows, st1, a_rd, AFS, i);
+      nb[i] = frag(kBRows, st1, b_rd, 1024, i);
       dma(stf, i, kt + kStages - 1);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
@@ -691,30 +701,41 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   }
   wait_vmcnt<(kStages - 2) * 2 * kW4Dma>();  // step 0 landed (own loads)
   block_barrier();                             // ... and every wave's
-  auto k_loop = [&](auto ng_c) {
+  auto k_loop = [&](auto ng_c, auto afs_c) {
+    constexpr uint32_t AFS = decltype(afs_c)::value;
     bf16x8 pa[8], pb[8], qa[8], qb[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      pa[f] = frag(kARows, lds0, a_rd, f);
-      pb[f] = frag(kBRows, lds0, b_rd, f);
+      pa[f] = frag(kARows, lds0, a_rd, AFS, f);
+      pb[f] = frag(kBRows, lds0, b_rd, 1024, f);
     }
-    step(ng_c, kTrue{}, 0, pa, pb, qa, qb);
+    step(ng_c, kTrue{}, afs_c, 0, pa, pb, qa, qb);
     int kt = 1;
     for (; kt + 1 < KT; kt += 2) {
-      step(ng_c, kFalse{}, kt, qa, qb, pa, pb);
-      step(ng_c, kFalse{}, kt + 1, pa, pb, qa, qb);
+      step(ng_c, kFalse{}, afs_c, kt, qa, qb, pa, pb);
+      step(ng_c, kFalse{}, afs_c, kt + 1, pa, pb, qa, qb);
     }
-    if (kt < KT) step(ng_c, kFalse{}, kt, qa, qb, pa, pb);
+    if (kt < KT) step(ng_c, kFalse{}, afs_c, kt, qa, qb, pa, pb);
   };
   // a segment's last tile, and the narrow layout, run fewer groups
-  if (ng == 8) k_loop(std::integral_constant<int, 8>{});
-  else if (ng == 6) k_loop(std::integral_constant<int, 6>{});
-  else if (ng == 4) k_loop(std::integral_constant<int, 4>{});
-  else if (ng == 2) k_loop(std::integral_constant<int, 2>{});
-  else k_loop(std::integral_constant<int, 0>{});
+  using Inter = std::integral_constant<uint32_t, 32 * 64>;
+  using Contig = std::integral_constant<uint32_t, 16 * 64>;
+  if (inter) {
+    if (ng == 8) k_loop(std::integral_constant<int, 8>{}, Inter{});
+    else if (ng == 6) k_loop(std::integral_constant<int, 6>{}, Inter{});
+    else if (ng == 4) k_loop(std::integral_constant<int, 4>{}, Inter{});
+    else if (ng == 2) k_loop(std::integral_constant<int, 2>{}, Inter{});
+    else k_loop(std::integral_constant<int, 0>{}, Inter{});
+  } else {
+    if (ng == 8) k_loop(std::integral_constant<int, 8>{}, Contig{});
+    else if (ng == 6) k_loop(std::integral_constant<int, 6>{}, Contig{});
+    else if (ng == 4) k_loop(std::integral_constant<int, 4>{}, Contig{});
+    else if (ng == 2) k_loop(std::integral_constant<int, 2>{}, Contig{});
+    else k_loop(std::integral_constant<int, 0>{}, Contig{});
+  }
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 
-  // ---- epilogue: lane holds row rbase + 16 i + li, columns cbase + 16 j +
+  // ---- epilogue: lane holds row r0 + rstep i + li, columns cbase + 16 j +
   // 4 lg .. +3.  The weight-gradient form stores its fp32 groups of 4
   // directly.  The bf16 forms pair tiles (2p, 2p + 1): even lg stores
   // columns 16 (2p) + 4 lg .. +7 (its own 4 and its partner's, lane l ^ 16),
@@ -730,7 +751,8 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
   const int li_e = lane_e & 15, lg_e = lane_e >> 4;
   const bool odd = lg_e & 1;
-  const int rbase_e = narrow ? wave * 64 : (wave >> 1) * 128;
+  const int r0_e = kTN ? (wave >> 1) * 128 : (narrow ? wave * 64 : 16 * (wave >> 1));
+  const int rstep_e = inter ? 32 : 16;
   const int cbase_e = narrow ? 0 : (wave & 1) * 128;
   // GELU' and accumulate read a bf16 tensor that may be C itself: every
   // value this lane needs is loaded before the first store (one memory
@@ -740,7 +762,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   if (kReads) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int m = rbase_e + 16 * i + li_e;
+      const int m = r0_e + rstep_e * i + li_e;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = n0 + cbase_e + 16 * j + 4 * lg_e;
@@ -753,7 +775,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int m = rbase_e + 16 * i + li_e;
+    const int m = r0_e + rstep_e * i + li_e;
     if (i >= ng || m >= rows) continue;  // uniform over the lane pair (l, l ^ 16)
     if (kTN) {
       float* crow = (float*)Cv + ((size_t)seg * M + row0 + m) * N;
