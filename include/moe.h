@@ -449,8 +449,11 @@ moe_status moe_expert_ffn_backward(const moe_shape* s, const void* xp, const int
  * plus the router's and the shared expert's input gradients,
  *   dx[t] = sum_{k kept} d_xp[row_of[t,k]] (+ d_x_shared[t])
  *           + d_logits[t] * W_r^T
- * (the first part summed in fp32 in slot order; in bf16 mode the last term
- * uses d_logits rounded to bf16).
+ * summed in fp32; in bf16 mode the last term uses d_logits rounded to bf16.
+ * In bf16 mode with at most 16 experts and H * pad8(E) * 2 <= 64 KiB, one
+ * kernel sums all three terms (router term, slots in order, shared term) and
+ * rounds once; otherwise the slots (in order) and the shared term are summed
+ * and rounded, and the router term is then accumulated by a GEMM.
  *
  *   d_xp      [max_rows,H]   from moe_expert_ffn_backward
  *   row_of    [T,K]

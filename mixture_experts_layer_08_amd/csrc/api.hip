@@ -543,10 +543,17 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
   a.T = s->T;
   a.H = s->H;
   a.K = s->K;
+  a.E = s->E;
+  const bool fused = permute_bwd_fuses_route(bf, s->H, s->E);
+  if (fused) {
+    a.d_logits = d_logits;
+    a.w_router = w_router;
+  }
   hipError_t e = launch_permute_bwd(a, hs);
-  // dx += d_logits W_r^T: an NT GEMM with K = E accumulating into dx; in bf16
-  // mode over copies padded to a multiple of 8 experts (16-byte rows)
-  if (e == hipSuccess) {
+  // Otherwise dx += d_logits W_r^T: an NT GEMM with K = E accumulating into
+  // dx; in bf16 mode over copies padded to a multiple of 8 experts (16-byte
+  // rows)
+  if (e == hipSuccess && !fused) {
     if (bf) {
       const int E8 = pad8(s->E);
       bf16* dl8 = at<bf16>(ws, L.dl8);

@@ -32,6 +32,14 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return v;
 }
 
+// c + a.lo * b.lo + a.hi * b.hi for bf16 pairs, accumulated in fp32
+// (v_dot2c_f32_bf16: the products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // Elements of a 16-byte vector as fp32 (8 bf16 or 4 fp32) and back.
 template <bool BF16>
 __device__ __forceinline__ float vec_elem(const u32x4& v, int i) {
@@ -430,6 +438,162 @@ __global__ __launch_bounds__(256) void k_permute_bwd(
   }
 }
 
+// The same un-permute with the router's input gradient folded in (bf16, at
+// most 16 experts):
+//   dx[t] = sum_{k kept} d_xp[row_of[t,k]] (+ d_x_shared[t])
+//           + sum_e bf16(d_logits[t,e]) W_r[:,e],
+// summed in fp32 (the router term first, expert pairs in order on the bf16
+// dot-product instruction, then the slots in order, then the shared term) and
+// rounded once.  Each workgroup first stages W_r [H][E] in LDS as
+// [h mod 8][e / 8][h / 8][8 experts] (zero past E): lane l of a wave then
+// reads the 16-byte expert row of its column h = 8c + i at consecutive
+// addresses, and the workgroup's tokens share one copy.  Wave w of workgroup
+// b takes tokens b*8 + w, then steps of 8 * grid.
+constexpr int kPermRouteThreads = 512, kPermRouteWaves = kPermRouteThreads / kWave;
+template <int NQ, int VPL>
+__global__ __launch_bounds__(kPermRouteThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_permute_bwd_route(
+    const u32x4* __restrict__ d_xp, const int32_t* __restrict__ row_of,
+    const u32x4* __restrict__ d_x_shared, const float* __restrict__ d_logits,
+    const uint16_t* __restrict__ w_router, u32x4* __restrict__ dx, int T, int nvec, int K,
+    int E, int w_vec16) {
+  extern __shared__ u32x4 w_lds[];  // [8][NQ][nvec] rows of 8 bf16
+  // Staging.  With 16-byte rows, kStage rows per thread are loaded before any
+  // is stored (indexes clamped to the last row), so their L2 latencies
+  // overlap; other widths gather the experts one by one.
+  constexpr int kStage = 8;
+  const int n_rows = 8 * NQ * nvec;
+  if (w_vec16) {  // E a multiple of 8 and W_r 16-byte aligned
+    for (int base = 0; base < n_rows; base += kStage * kPermRouteThreads) {
+      u32x4 v[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int idx = min(base + u * kPermRouteThreads + (int)threadIdx.x, n_rows - 1);
+        const int c = idx % nvec, pq = idx / nvec;  // pq = i * NQ + q
+        v[u] = *(const u32x4*)(w_router + (size_t)(8 * c + pq / NQ) * E + 8 * (pq % NQ));
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int idx = base + u * kPermRouteThreads + (int)threadIdx.x;
+        if (idx < n_rows) w_lds[idx] = v[u];
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < n_rows; idx += kPermRouteThreads) {
+      const int c = idx % nvec, pq = idx / nvec;
+      const int h = 8 * c + pq / NQ, e0 = 8 * (pq % NQ);
+      uint32_t lo[8];
+#pragma unroll
+      for (int ee = 0; ee < 8; ++ee)
+        lo[ee] = e0 + ee < E ? w_router[(size_t)h * E + e0 + ee] : 0u;
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = lo[2 * q] | (lo[2 * q + 1] << 16);
+      w_lds[idx] = v;
+    }
+  }
+  __syncthreads();  // the only barrier: every wave reaches it before its token loop
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Lane l < K holds the token's l-th row and lane e < E its logit gradient;
+  // the next token's are requested before this one's rows.
+  const int stride = gridDim.x * kPermRouteWaves;
+  int t = blockIdx.x * kPermRouteWaves + wave;
+  int row_n = -1;
+  float dl_n = 0.0f;
+  if (t < T) {
+    if (lane < K) row_n = row_of[(size_t)t * K + lane];
+    if (lane < E) dl_n = d_logits[(size_t)t * E + lane];
+  }
+  for (; t < T; t += stride) {
+    const int row = row_n;
+    const float dlv = dl_n;
+    if (t + stride < T) {
+      if (lane < K) row_n = row_of[(size_t)(t + stride) * K + lane];
+      if (lane < E) dl_n = d_logits[(size_t)(t + stride) * E + lane];
+    }
+    int rows[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rows[k] = __builtin_amdgcn_readlane(row, k);
+    uint32_t dl2[4 * NQ];  // bf16(d_logits[t]) in expert pairs, zero past E
+#pragma unroll
+    for (int p = 0; p < 4 * NQ; ++p)
+      dl2[p] = pack_bf16x2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(dlv), 2 * p)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dlv), 2 * p + 1)));
+    for (int c0 = 0; c0 < nvec; c0 += 64 * VPL) {
+      // The first two slots' rows are requested first (zero where dropped);
+      // the router term, which needs only LDS, runs while they are in flight.
+      u32x4 v01[2][VPL];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) v01[k][j] = u32x4{0u, 0u, 0u, 0u};
+        if (k < K && rows[k] >= 0) {
+          const u32x4* src = d_xp + (size_t)rows[k] * nvec;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int c = c0 + lane + 64 * j;
+            if (c < nvec) v01[k][j] = src[c];
+          }
+        }
+      }
+      float acc[VPL][8];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int c = min(c0 + lane + 64 * j, nvec - 1);  // columns past H are not stored
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[j][i] = 0.0f;
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const u32x4 w = w_lds[(i * NQ + q) * nvec + c];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) acc[j][i] = dot2_bf16(w[p], dl2[4 * q + p], acc[j][i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[j][i] += vec_elem<true>(v01[k][j], i);
+#pragma unroll
+      for (int k = 2; k < 8; ++k) {
+        if (k < K && rows[k] >= 0) {
+          const u32x4* src = d_xp + (size_t)rows[k] * nvec;
+          u32x4 v[VPL];
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int c = c0 + lane + 64 * j;
+            if (c < nvec) v[j] = src[c];
+          }
+#pragma unroll
+          for (int j = 0; j < VPL; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] += vec_elem<true>(v[j], i);
+        }
+      }
+      if (d_x_shared) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = c0 + lane + 64 * j;
+          if (c < nvec) {
+            const u32x4 v = d_x_shared[(size_t)t * nvec + c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] += vec_elem<true>(v, i);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int c = c0 + lane + 64 * j;
+        if (c < nvec) dx[(size_t)t * nvec + c] = vec_pack<true>(acc[j]);
+      }
+    }
+  }
+}
+
 // dst [R][Ep] bf16 = src [R][E] (fp32 or bf16), zero in columns E..Ep-1.
 template <bool SRC_F32>
 __global__ __launch_bounds__(256) void k_pad_bf16(const void* __restrict__ src,
@@ -518,8 +682,30 @@ hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool permute_bwd_fuses_route(bool bf16, int H, int E) {
+  const int e8 = (E + 7) / 8 * 8;
+  return bf16 && e8 <= 16 && (long long)H * e8 * 2 <= kPermuteRouteLds;
+}
+
 hipError_t launch_permute_bwd(const PermuteBwdArgs& a, hipStream_t st) {
   const int nvec = a.H * (a.bf16 ? 2 : 4) / 16;
+  if (a.d_logits) {
+    if (!permute_bwd_fuses_route(a.bf16, a.H, a.E) || !a.w_router) return hipErrorInvalidValue;
+    const int nq = (a.E + 7) / 8;
+    const size_t lds = (size_t)a.H * nq * 16;
+    // two workgroups of eight waves per CU at 64 KiB of LDS each
+    const int grid = std::min((a.T + kPermRouteWaves - 1) / kPermRouteWaves, 2 * 256);
+    const int vec16 = a.E % 8 == 0 && ((uintptr_t)a.w_router & 15) == 0;
+    if (nq == 1)
+      k_permute_bwd_route<1, 4><<<grid, kPermRouteThreads, lds, st>>>(
+          (const u32x4*)a.d_xp, a.row_of, (const u32x4*)a.d_x_shared, a.d_logits,
+          (const uint16_t*)a.w_router, (u32x4*)a.dx, a.T, nvec, a.K, a.E, vec16);
+    else
+      k_permute_bwd_route<2, 4><<<grid, kPermRouteThreads, lds, st>>>(
+          (const u32x4*)a.d_xp, a.row_of, (const u32x4*)a.d_x_shared, a.d_logits,
+          (const uint16_t*)a.w_router, (u32x4*)a.dx, a.T, nvec, a.K, a.E, vec16);
+    return hipGetLastError();
+  }
   const int grid = (a.T + 3) / 4;
   if (a.bf16)
     k_permute_bwd<true, 8><<<grid, 256, 0, st>>>((const u32x4*)a.d_xp, a.row_of,

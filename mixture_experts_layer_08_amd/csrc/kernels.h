@@ -233,13 +233,21 @@ struct RouteBwdArgs {
 };
 hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
 
+// dx = the kept slots' d_xp rows (+ d_x_shared); with d_logits set, also
+// + bf16(d_logits) W_r^T in the same pass (only where
+// permute_bwd_fuses_route holds: bf16, at most 16 experts, W_r within
+// kPermuteRouteLds bytes of LDS once padded to a multiple of 8 experts).
+constexpr long long kPermuteRouteLds = 64 * 1024;
+bool permute_bwd_fuses_route(bool bf16, int H, int E);
 struct PermuteBwdArgs {
   bool bf16;
   const void* d_xp;
   const int32_t* row_of;
   const void* d_x_shared;  // nullable
+  const float* d_logits;   // nullable: no router term
+  const void* w_router;    // [H][E] in the layer dtype, with d_logits
   void* dx;
-  int T, H, K;
+  int T, H, K, E;
 };
 hipError_t launch_permute_bwd(const PermuteBwdArgs& a, hipStream_t st);
 

@@ -391,6 +391,25 @@ def combine_backward(dy, out, row_of, w):
     return dout, dw
 
 
+def permute_backward(dxp, row_of, d_logits_raw, w_r, dxs=None):
+    """dx, the input gradient: the adjoint of :func:`permute` (each kept row's
+    gradient returns to its token), plus the router's term d_logits W_r^T
+    (the logits are x W_r + b), plus the shared expert's input gradient when
+    there is one.
+    """
+    dxp = np.asarray(dxp, dtype=np.float64)
+    T, K = row_of.shape
+    dx = np.zeros((T, dxp.shape[1]), dtype=np.float64)
+    for k in range(K):
+        r = row_of[:, k]
+        m = r >= 0
+        dx[m] += dxp[r[m]]
+    dx += np.asarray(d_logits_raw, dtype=np.float64) @ np.asarray(w_r, dtype=np.float64).T
+    if dxs is not None:
+        dx += np.asarray(dxs, dtype=np.float64)
+    return dx
+
+
 def route_backward(logits, ids, w, dw, E: int, K: int, alpha: float):
     """d L / d logits from the routing weights and from alpha * aux.
 
@@ -441,22 +460,15 @@ def backward(x, w_r, b_r, w1, w2, ws1=None, ws2=None, *, dy, K: int, cf: float,
         a, b = int(offsets[e]), int(offsets[e + 1])
         if b > a:
             dxp[a:b], dw1[e], dw2[e] = ffn_backward(fw["xp"][a:b], w1[e], w2[e], dout[a:b])
-    # un-permute: each kept row's gradient returns to its token
-    dx = np.zeros_like(x64)
-    for k in range(K):
-        r = row_of[:, k]
-        m = r >= 0
-        dx[m] += dxp[r[m]]
     l_sel = np.asarray(logits, dtype=np.float64) if logits is not None \
         else fw["logits_oracle"].astype(np.float32).astype(np.float64)
     dl = route_backward(l_sel, fw["ids"], fw["w"], dw, E, K, alpha)
     dl_raw = dl / float(tau)
-    dx += dl_raw @ np.asarray(w_r, dtype=np.float64).T
     dw_r = x64.T @ dl_raw
     db_r = dl_raw.sum(axis=0)
-    dws1 = dws2 = None
+    dxs = dws1 = dws2 = None
     if ws1 is not None:
         dxs, dws1, dws2 = ffn_backward(x64, ws1, ws2, dy)
-        dx += dxs
+    dx = permute_backward(dxp, row_of, dl_raw, w_r, dxs)
     return dict(dx=dx, dw_r=dw_r, db_r=db_r, dw1=dw1, dw2=dw2, dws1=dws1, dws2=dws2,
                 d_out=dout, d_w=dw, d_xp=dxp, d_logits=dl, forward=fw)

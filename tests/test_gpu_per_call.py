@@ -1,5 +1,6 @@
-"""Per-call parity: moe_expert_ffn and moe_combine alone, on inputs the test
-builds itself, against the oracle's function for the same step.
+"""Per-call parity: moe_expert_ffn, moe_combine and moe_permute_backward
+alone, on inputs the test builds itself, against the oracle's function for
+the same step.
 
   * moe_expert_ffn on a packed buffer whose segment sizes are chosen directly
     (empty segments, 1 row, 255 / 256 / 257 rows around the 256-row tile,
@@ -7,7 +8,10 @@ builds itself, against the oracle's function for the same step.
     against oracle.expert_ffn and oracle.ffn;
   * moe_combine on random expert outputs and an arbitrary row map with
     dropped slots (-1) and repeated rows, with and without a shared output,
-    against oracle.combine.
+    against oracle.combine;
+  * moe_permute_backward on random row gradients, a row map with dropped
+    slots, router gradients and weights, with and without a shared expert's
+    input gradient, against oracle.permute_backward.
 
 Tolerances are those of the layer (max |got - ref| / max |ref|: 2e-2 in bf16
 mode, 1e-4 in fp32 mode).
@@ -138,3 +142,52 @@ def test_combine_alone(dtype, shared):
     print(f"[combine alone {dtype} shared={shared}] max rel err {err:.2e}", flush=True)
     assert err <= TOL[dtype]
     assert not torch.any(y[7] != (sh[7] if shared else 0))
+
+
+# (dtype, T, H, E, K, shared): bf16 with at most 16 experts folds d_logits W_r^T
+# into the un-permute kernel (router weights staged in LDS, at most 64 KiB
+# once padded to 8 experts); wider routers, fp32 mode and larger H run it as
+# a separate accumulating GEMM.
+PERMUTE_BWD = [
+    ("bf16", 5000, 4096, 8, 2, False),   # 64 KiB of weights, more tokens than one sweep
+    ("bf16", 700, 2048, 16, 4, True),    # two 8-expert planes, 64 KiB
+    ("bf16", 333, 1336, 12, 3, False),   # E not a multiple of 8: scalar staging
+    ("bf16", 129, 264, 1, 1, True),      # one expert
+    ("bf16", 300, 4160, 8, 2, False),    # above the LDS limit: GEMM form
+    ("bf16", 250, 256, 32, 4, True),     # more than 16 experts: GEMM form
+    ("f32", 300, 264, 8, 2, True),
+]
+
+
+@pytest.mark.parametrize("dtype,T,H,E,K,shared", PERMUTE_BWD,
+                         ids=lambda v: str(v))
+def test_permute_backward_alone(dtype, T, H, E, K, shared):
+    """dx = sum of the kept slots' d_xp rows (+ the shared expert's dx)
+    + d_logits W_r^T, against oracle.permute_backward."""
+    w = Workload("permute_bwd_alone", T=T, H=H, E=E, K=K, h=64, hs=64 if shared else 0,
+                 cf=0.0, dtype=dtype)
+    buf = layer.MoeBuffers.allocate(w, train=True)
+    dt = w.torch_dtype()
+    N = T * K
+    r = np.random.default_rng(T + H + E)
+    row_of = r.permutation(N).reshape(T, K).astype(np.int32)
+    row_of[r.random((T, K)) < 0.15] = -1
+    row_of[T // 2] = -1  # a token with every slot dropped
+    g = torch.Generator(device="cuda").manual_seed(H)
+    d_xp = torch.randn((N, H), generator=g, device="cuda").to(dt)
+    dxs = torch.randn((T, H), generator=g, device="cuda").to(dt) if shared else None
+    d_logits = torch.randn((T, E), generator=g, device="cuda") * 0.5
+    w_r = (torch.randn((H, E), generator=g, device="cuda") * 0.05).to(dt)
+    dx = torch.full((T, H), float("nan"), dtype=dt, device="cuda")
+    print(f"[permute backward alone {dtype} T={T} H={H} E={E} K={K} shared={shared}]",
+          flush=True)
+    B.moe_permute_backward(buf.shape, d_xp, torch.from_numpy(row_of).cuda(), dxs, d_logits,
+                           w_r, dx, buf.ws)
+    torch.cuda.synchronize()
+    ref = O.permute_backward(f64(d_xp), row_of.astype(np.int64), f64(d_logits), f64(w_r),
+                             f64(dxs) if shared else None)
+    got = f64(dx)
+    assert np.all(np.isfinite(got)), "rows of dx left unwritten"
+    err = relerr(got, ref)
+    print(f"  max rel err {err:.2e}", flush=True)
+    assert err <= TOL[dtype]
