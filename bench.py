@@ -206,7 +206,7 @@ def mxfp8_leg(w, p, dev, steps: int, warmup: int) -> dict:
         "steps": steps,
         "stages_ms": {"route": route_ms, "aux_loss": aux_ms, "permute_mxfp8": perm_ms,
                       "expert_ffn_mxfp8": ffn_ms, "combine_mxfp8": comb_ms},
-        "grouped_gemm": {"kernel": "k_grouped_gemm_mx8", "bound": "mfma", "achieved": tflops,
+        "grouped_gemm": {"kernel": "k_grouped_gemm_mx8w4", "bound": "mfma", "achieved": tflops,
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": tflops / PEAK_FP8_TFLOPS, "flop_per_launch": flop / launches,
                          "traffic": traffic_from_profile(w.name, "mx8"),

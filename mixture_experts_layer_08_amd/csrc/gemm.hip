@@ -115,6 +115,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   constexpr bool kTN = LAYOUT == kGemmTN;
   constexpr bool kARows = !kTN;               // A in "rows" form
   constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
+  // Prefetch distance in K-steps (see the schedule below).
+  constexpr int kDist = LAYOUT == kGemmNN ? 2 : 3;
+  static_assert(kDist + 1 <= kStages, "a refill needs a free slot");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
   int mt, nt, seg, row0, rows;
@@ -487,10 +490,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // otherwise put the rows k and k + 8 of one read on the same banks.
 //
 // Per K-step: wait until step kt+1 has landed for every wave (s_waitcnt on
-// the own loads, then the barrier, which also frees step kt-1's slot), then
-// 64 MFMAs on fragments read during the previous step, in 8 groups of 8;
-// group i also reads fragment i of both operands for step kt+1 and issues
-// refill load i.  A fragment is 8 consecutive k (k chunk l / 16) of one row
+// the own loads, then the barrier), then 64 MFMAs on fragments read during
+// the previous step, in 8 groups of 8; group i also reads fragment i of both
+// operands for step kt+1 and issues refill load i of step kt + D + 1, D the
+// prefetch distance.  D = 2 (row-major form) refills slot kt - 1, which every
+// wave finished reading during step kt - 2.  D = 3 (transposed forms of the
+// backward, whose loads arrive later) refills slot kt itself, read during
+// step kt - 1: each wave first waits for its own LDS reads (lgkmcnt 0), then
+// the barrier.  Measured: D = 3 takes the expert backward from 25.3 to
+// 24.7 ms, and costs the forward 1% (the exposed wait for the last
+// fragment reads).  A fragment is 8 consecutive k (k chunk l / 16) of one row
 // or column (l % 16) per lane.  With the operands swapped, lane l holds row
 // l % 16 and columns 4 (l / 16) .. +3 of each 16 x 16 output tile.
 //
@@ -663,10 +672,11 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
                   const bf16x8* cb, bf16x8* na, bf16x8* nb) {
     constexpr int NG = decltype(ng_c)::value;
     constexpr uint32_t AFS = decltype(afs_c)::value;  // A fragment stride (rows form)
-    wait_vmcnt<(kStages - 3) * 2 * kW4Dma>();
+    wait_vmcnt<(kDist - 1) * 2 * kW4Dma>();  // younger than step kt+1: kDist - 1 steps
+    if (kDist == 3) wait_lgkm0();  // this wave's reads of slot kt (refilled below) are done
     block_barrier();
     const uint32_t st1 = stage_addr(kt + 1);
-    const uint32_t stf = stage_addr(kt + kStages - 1);
+    const uint32_t stf = stage_addr(kt + kDist + 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < NG) {
@@ -679,7 +689,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
       }
       na[i] = frag(kARows, st1, a_rd, AFS, i);
       nb[i] = frag(kBRows, st1, b_rd, 1024, i);
-      dma(stf, i, kt + kStages - 1);
+      dma(stf, i, kt + kDist + 1);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -694,12 +704,12 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // These vmcnt counts hold only while the LDS-direct loads are the loop's
   // only vector-memory instructions: the build refuses a spill.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
+  for (int s = 0; s <= kDist; ++s) {
     const uint32_t st = stage_addr(s);
 #pragma unroll
     for (int d = 0; d < 2 * kW4Dma; ++d) dma(st, d, s);
   }
-  wait_vmcnt<(kStages - 2) * 2 * kW4Dma>();  // step 0 landed (own loads)
+  wait_vmcnt<kDist * 2 * kW4Dma>();  // step 0 landed (own loads)
   block_barrier();                             // ... and every wave's
   auto k_loop = [&](auto ng_c, auto afs_c) {
     constexpr uint32_t AFS = decltype(afs_c)::value;

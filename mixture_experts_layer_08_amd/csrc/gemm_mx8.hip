@@ -12,9 +12,12 @@
 // from the accumulators, so no separate quantise pass reads it back (the
 // cost warning of section 5.4).
 //
-// Design (gfx950): the bf16 kernel's 256 x 256 tile on eight waves (two per
-// SIMD), each wave a 128 x 64 block of 4 x 2 v_mfma_scale_f32_32x32x64_f8f6f4
-// tiles; one K-step is 64 values = 64 bytes per row, so a stage holds the same
+// Design (gfx950): two kernels on the bf16 kernels' 256 x 256 tile.  The
+// four-wave k_grouped_gemm_mx8w4 (below the eight-wave one) is the one the
+// launcher runs; building with MOE_MX8_W4=0 selects the eight-wave form
+// described here: eight waves (two per SIMD), each wave a 128 x 64 block of
+// 4 x 2 v_mfma_scale_f32_32x32x64_f8f6f4 tiles; one K-step is 64 values = 64
+// bytes per row, so a stage holds the same
 // 32 KiB (A [256][64 B], B [256][64 B], 16-byte chunk c of row r stored at
 // c ^ ((r >> 2) & 3)), filled by LDS-direct loads through a 4-stage ring.
 // The block scales ride in the same ring: every even step's stage also
@@ -312,9 +315,257 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Four-wave form: the same tile, stage layout, ring and epilogue, with one
+// wave per SIMD owning a 128 x 128 block as 4 x 4 scaled 32x32x64 tiles (256
+// fp32 accumulators per lane, in AGPRs).  A K-step then reads 64 KiB of
+// fragments from LDS per CU instead of the eight-wave layout's 96 KiB (with
+// the 32 KiB the LDS-direct loads write, the eight-wave kernel keeps the LDS
+// busy for about as long as its MFMAs run), and the four waves hide their
+// own latencies.  Per K-step: wait until step kt+1 has landed for every wave
+// (own loads by vmcnt, own LDS reads by lgkmcnt, then the barrier), then the
+// 16 MFMAs on fragments read during the previous step, in 4 groups; group i
+// runs two MFMAs, reads the A fragment i of step kt+1, issues A refill load
+// i, runs two more, reads B fragment i and issues B refill load i.  The
+// refills are for step kt+4 into slot kt % 4 itself, whose fragments every
+// wave read during step kt-1: three steps of latency cover for each load.
+// The scale words of a step pair are read early in the step before the pair
+// and their bytes extracted at the start of each step.
+//
+// Measured against the eight-wave kernel (mixtral-sized MXFP8 forward, A/B
+// on one box): 6.41 vs 6.47 ms for both GEMMs, at a higher clock (1.9 vs
+// 1.7-1.8 GHz: less LDS traffic) but fewer MFMA-busy cycles (57-63% vs
+// 60-70%).  Counter runs of the earlier forms: two loads back to back per
+// group of four MFMAs, 6.74 ms; spread as above, 6.58 ms; the refill
+// distance of two steps left the waves waiting 21% of their cycles, three
+// steps 17%.
+constexpr int kMxW4Threads = 256;
+constexpr int kMxW4Dma = 4;  // data LDS-direct loads per operand, per wave, per stage
+
+template <int EPI>
+__global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, uint8_t* __restrict__ C,
+    uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int G, int fixed_rows,
+    int a_rows, int a_ld, int c_ld, int mt_bound, int Kd, int N, int xcd_chunk) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_mx4[];
+  const int nt_count = (N + kMxBN - 1) / kMxBN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
+  if (tile >= mt_bound * nt_count) return;
+  int mt, nt, seg, row0, rows;
+  decode_tile(tile, mt_bound, nt_count, mt, nt);
+  if (!find_segment<kMxBM>(offsets, G, fixed_rows, mt, seg, row0, rows)) return;
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rr = lane & 31, kh = lane >> 5;
+  const int n0 = nt * kMxBN;
+  const int nslab = (Kd + 127) / 128;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem_mx4;
+
+  // ---- global -> LDS loaders ----
+  // data: load d of this wave covers stage rows 16 (4d + wave) .. +15, four
+  // lanes per 64-byte row; rows past the buffer read as zero.  Scales: this
+  // wave loads the words of A rows 64 wave .. +63 and of B rows 64 wave ..
+  // +63 (lane l: row .. + l) of slab kt / 2.
+  const int r_row_l = lane >> 2;
+  const int r_chunk = mx_swz(r_row_l, lane & 3);
+  const u32x4 ra = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd);
+  const u32x4 rb = make_rsrc_words(B + ((size_t)seg * nt_count + nt) * kMxBN * (size_t)Kd,
+                                   (long long)kMxBN * Kd);
+  const uint32_t b_off = (uint32_t)((r_row_l + 16 * wave) * kMxBK + r_chunk * 16);
+  const uint32_t d_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 16);
+  const uint32_t d_stride = (uint32_t)(4 * 16 * Kd);
+  const u32x4 rsa = make_rsrc_words(As, (long long)nslab * a_ld * 4);
+  const u32x4 rsb = make_rsrc_words(Bs + (size_t)seg * nslab * N * 4, (long long)nslab * N * 4);
+  const uint32_t sa_off = (uint32_t)(row0 + 64 * wave + lane) * 4;
+  const uint32_t sb_off = (uint32_t)(n0 + 64 * wave + lane) * 4;
+  const uint32_t sa_slab = (uint32_t)a_ld * 4, sb_slab = (uint32_t)N * 4;
+
+  auto stage_addr = [&](int kt) {
+    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt & (kMxStages - 1)) * kMxStageBytes);
+  };
+  // load d of step kt: 0-3 A, 4-7 B, 8 and 9 the A and B scale words (even
+  // steps only)
+  auto dma = [&](uint32_t st, int d, int kt) {
+    const bool in_k = kt * kMxBK < Kd;
+    if (d < kMxW4Dma) {
+      dma_load16(st + (4 * d + wave) * 1024,
+                 in_k ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
+    } else if (d < 2 * kMxW4Dma) {
+      const int e = d - kMxW4Dma;
+      dma_load16(st + kMxBM * kMxBK + (4 * e + wave) * 1024,
+                 in_k ? b_off + e * (4 * 16 * kMxBK) + (uint32_t)kt * (kMxBN * kMxBK) : kOob, rb);
+    } else if (d == 2 * kMxW4Dma) {
+      dma_load4(st + kMxDataBytes + wave * 256,
+                in_k ? sa_off + (uint32_t)(kt >> 1) * sa_slab : kOob, rsa);
+    } else {
+      dma_load4(st + kMxDataBytes + 1024 + wave * 256,
+                in_k ? sb_off + (uint32_t)(kt >> 1) * sb_slab : kOob, rsb);
+    }
+  };
+  auto issue_step = [&](int kt) {
+    const uint32_t st = stage_addr(kt);
+#pragma unroll
+    for (int d = 0; d < 2 * kMxW4Dma; ++d) dma(st, d, kt);
+    if ((kt & 1) == 0) {
+      dma(st, 2 * kMxW4Dma, kt);
+      dma(st, 2 * kMxW4Dma + 1, kt);
+    }
+  };
+
+  // ---- LDS -> register fragments: tile i of the wave's rows is rows
+  // wm 128 + 32 i + rr (+ 2 KiB per i), chunks kh and kh + 2 ----
+  const int ra_row = wm * 128 + rr, rb_row = wn * 128 + rr;
+  const uint32_t a_rd0 = (uint32_t)ra_row * kMxBK + (uint32_t)mx_swz(ra_row, kh) * 16;
+  const uint32_t a_rd1 = (uint32_t)ra_row * kMxBK + (uint32_t)mx_swz(ra_row, kh + 2) * 16;
+  const uint32_t b_rd0 = kMxBM * kMxBK + (uint32_t)rb_row * kMxBK + (uint32_t)mx_swz(rb_row, kh) * 16;
+  const uint32_t b_rd1 = kMxBM * kMxBK + (uint32_t)rb_row * kMxBK + (uint32_t)mx_swz(rb_row, kh + 2) * 16;
+  const uint32_t sa_rd = kMxDataBytes + (uint32_t)ra_row * 4;
+  const uint32_t sb_rd = kMxDataBytes + 1024 + (uint32_t)rb_row * 4;
+  auto read_a = [&](uint32_t st, int i) {
+    return frag(lds_b128(st + a_rd0 + i * 32 * kMxBK), lds_b128(st + a_rd1 + i * 32 * kMxBK));
+  };
+  auto read_b = [&](uint32_t st, int j) {
+    return frag(lds_b128(st + b_rd0 + j * 32 * kMxBK), lds_b128(st + b_rd1 + j * 32 * kMxBK));
+  };
+
+  f32x16 acc[4][4];  // set by the first step's MFMAs (zero C operand)
+  uint32_t wa[4], wb[4];
+  auto step = [&](auto par, auto first_c, int kt, const i32x8* ca, const i32x8* cb, i32x8* na,
+                  i32x8* nb) {
+    constexpr int P = decltype(par)::value;  // kt & 1
+    // younger than step kt+1: steps kt+2 and kt+3 (one of them even)
+    wait_vmcnt<4 * kMxW4Dma + 2>();
+    wait_lgkm0();  // this wave's reads of slot kt % 4 (refilled below) are done
+    block_barrier();
+
+    int sa[4], sb[4];  // this step's scale bytes: byte 2 P + kh of each word
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = (int)((wa[i] >> (8 * (2 * P + kh))) & 0xffu);
+      sb[i] = (int)((wb[i] >> (8 * (2 * P + kh))) & 0xffu);
+    }
+    const uint32_t st1 = stage_addr(kt + 1);
+    const uint32_t stf = stage_addr(kt + kMxStages);
+    if (P == 1) {  // step kt+1 starts a pair: its scale words, early
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wa[i] = lds_b32(st1 + sa_rd + i * 128);
+        wb[i] = lds_b32(st1 + sb_rd + i * 128);
+      }
+    }
+    auto mm = [&](int i, int j) {
+      if (decltype(first_c)::value)
+        acc[i][j] = mfma_mx8(cb[j], ca[i], f32x16{}, sb[j], sa[i]);
+      else
+        acc[i][j] = mfma_mx8(cb[j], ca[i], acc[i][j], sb[j], sa[i]);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mm(i, 0);
+      mm(i, 1);
+      na[i] = read_a(st1, i);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      dma(stf, i, kt + kMxStages);
+      mm(i, 2);
+      mm(i, 3);
+      nb[i] = read_b(st1, i);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      dma(stf, kMxW4Dma + i, kt + kMxStages);
+    }
+    if (P == 0) {
+      dma(stf, 2 * kMxW4Dma, kt + kMxStages);  // step kt+4 is even
+      dma(stf, 2 * kMxW4Dma + 1, kt + kMxStages);
+    }
+  };
+  using kTrue = std::integral_constant<bool, true>;
+  using kFalse = std::integral_constant<bool, false>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // The counts assume these LDS-direct loads are the only vector-memory
+  // instructions in the loop: the build refuses a spill, and so does the
+  // launcher.
+  const int KT = Kd / kMxBK;
+  issue_step(0);
+  issue_step(1);
+  issue_step(2);
+  issue_step(3);
+  wait_vmcnt<6 * kMxW4Dma + 2>();  // step 0 landed: younger are steps 1, 2 (+2), 3
+  block_barrier();
+  i32x8 pa[4], pb[4], qa[4], qb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pa[i] = read_a(lds0, i);
+    pb[i] = read_b(lds0, i);
+    wa[i] = lds_b32(lds0 + sa_rd + i * 128);
+    wb[i] = lds_b32(lds0 + sb_rd + i * 128);
+  }
+  step(P0{}, kTrue{}, 0, pa, pb, qa, qb);
+  int kt = 1;
+  for (; kt + 1 < KT; kt += 2) {
+    step(P1{}, kFalse{}, kt, qa, qb, pa, pb);
+    step(P0{}, kFalse{}, kt + 1, pa, pb, qa, qb);
+  }
+  if (kt < KT) step(P1{}, kFalse{}, kt, qa, qb, pa, pb);
+  wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
+
+  // ---- epilogue, per 32 x 32 tile as in the eight-wave kernel ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + i * 32 + rr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 128 + j * 32;  // first column of this tile's block
+      float v[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        v[r] = EPI == kMxEpiGeluQuantOperand ? gelu_tanh_f32(acc[i][j][r]) : acc[i][j][r];
+        amax = fmaxf(amax, fabsf(v[r]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const uint32_t code = mx_scale_code(amax);
+      const float inv = mx_inv_scale(code);
+      uint32_t d[4];  // columns 8g + 4kh .. +3 of the block
+#pragma unroll
+      for (int g = 0; g < 4; ++g) d[g] = mx_encode4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], inv);
+      const uint32_t x0 = __shfl_xor(kh ? d[0] : d[2], 32, kWave);
+      const uint32_t x1 = __shfl_xor(kh ? d[1] : d[3], 32, kWave);
+      const u32x4 o = kh ? u32x4{x0, d[2], x1, d[3]} : u32x4{d[0], x0, d[1], x1};
+      if (m < rows && nb < N) {
+        *(u32x4*)(C + (size_t)(row0 + m) * N + nb + 16 * kh) = o;
+        if (kh == 0) {
+          if (EPI == kMxEpiQuantRows)
+            Cs[(size_t)(row0 + m) * (N / kMxBlock) + nb / kMxBlock] = (uint8_t)code;
+          else
+            Cs[mx_operand_scale_index(c_ld, row0 + m, nb / kMxBlock)] = (uint8_t)code;
+        }
+      }
+    }
+  }
+}
+
+#ifndef MOE_MX8_W4
+#define MOE_MX8_W4 1
+#endif
+
 template <int EPI>
 static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
-  const hipError_t e = allow_dynamic_lds<k_grouped_gemm_mx8<EPI>, true>();
+  const hipError_t e = MOE_MX8_W4 ? allow_dynamic_lds<k_grouped_gemm_mx8w4<EPI>, true>()
+                                  : allow_dynamic_lds<k_grouped_gemm_mx8<EPI>, true>();
   if (e != hipSuccess) return e;
   if (a.Kd <= 0 || a.Kd % kMxBK != 0 || a.N <= 0 || a.N % kMxBlock != 0) return hipErrorInvalidValue;
   const int ntc = (a.N + kMxBN - 1) / kMxBN;
@@ -323,9 +574,14 @@ static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
   const long long grid = (long long)mtb * ntc;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  k_grouped_gemm_mx8<EPI><<<(unsigned)grid, kMxThreads, kMxSmem, st>>>(
-      a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
-      a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
+  if (MOE_MX8_W4)
+    k_grouped_gemm_mx8w4<EPI><<<(unsigned)grid, kMxW4Threads, kMxSmem, st>>>(
+        a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
+        a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
+  else
+    k_grouped_gemm_mx8<EPI><<<(unsigned)grid, kMxThreads, kMxSmem, st>>>(
+        a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
+        a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
   return hipGetLastError();
 }
 

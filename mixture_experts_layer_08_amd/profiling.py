@@ -40,7 +40,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 #   mx8:  the MXFP8 grouped GEMM (both epilogues)
 KERNELS = {
     "bf16": (re.compile(r"k_grouped_gemm_w4<\s*0\s*,"), ("gemm.hip", "gemm_common.h")),
-    "mx8": (re.compile(r"k_grouped_gemm_mx8<"), ("gemm_mx8.hip", "gemm_common.h", "mx.h")),
+    "mx8": (re.compile(r"k_grouped_gemm_mx8w4<"), ("gemm_mx8.hip", "gemm_common.h", "mx.h")),
 }
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
@@ -167,8 +167,8 @@ def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz:
         fraction of dense MFMA peak."""
     pats = {"k_grouped_gemm_w4 (GEMM1, GELU)": r"k_grouped_gemm_w4<\s*0\s*,\s*1>",
             "k_grouped_gemm_w4 (GEMM2)": r"k_grouped_gemm_w4<\s*0\s*,\s*0>",
-            "k_grouped_gemm_mx8 (GEMM1, GELU)": r"k_grouped_gemm_mx8<1>",
-            "k_grouped_gemm_mx8 (GEMM2)": r"k_grouped_gemm_mx8<0>",
+            "k_grouped_gemm_mx8w4 (GEMM1, GELU)": r"k_grouped_gemm_mx8w4<1>",
+            "k_grouped_gemm_mx8w4 (GEMM2)": r"k_grouped_gemm_mx8w4<0>",
             "k_permute (memory-bound)": r"k_permute<",
             "k_combine (memory-bound)": r"k_combine<"}
     per = collections.defaultdict(dict)
