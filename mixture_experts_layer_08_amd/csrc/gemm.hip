@@ -115,9 +115,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   constexpr bool kTN = LAYOUT == kGemmTN;
   constexpr bool kARows = !kTN;               // A in "rows" form
   constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
-  // Prefetch distance in K-steps (see the schedule below).
-  constexpr int kDist = LAYOUT == kGemmNN ? 2 : 3;
-  static_assert(kDist + 1 <= kStages, "a refill needs a free slot");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
   int mt, nt, seg, row0, rows;
@@ -517,6 +514,9 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   constexpr bool kTN = LAYOUT == kGemmTN;
   constexpr bool kARows = !kTN;               // A in "rows" form
   constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
+  // Prefetch distance in K-steps (see the schedule below).
+  constexpr int kDist = LAYOUT == kGemmNN ? 2 : 3;
+  static_assert(kDist + 1 <= kStages, "a refill needs a free slot");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int nt_count = (N + BN2 - 1) / BN2;
   int mt, nt, seg, row0, rows;

@@ -342,6 +342,13 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
 constexpr int kMxW4Threads = 256;
 constexpr int kMxW4Dma = 4;  // data LDS-direct loads per operand, per wave, per stage
 
+// Stage: data, then the A and the B scale words (2 KiB each: a tile's 256
+// rows start up to 3 words into the block).
+constexpr uint32_t kMx4AScale = kMxDataBytes, kMx4BScale = kMxDataBytes + 2048;
+constexpr uint32_t kMx4StageBytes = kMxDataBytes + 4096;
+constexpr size_t kMx4Smem = (size_t)kMxStages * kMx4StageBytes;  // 144 KiB
+static_assert(kMx4Smem <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
 template <int EPI>
 __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
@@ -369,9 +376,14 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
 
   // ---- global -> LDS loaders ----
   // data: load d of this wave covers stage rows 16 (4d + wave) .. +15, four
-  // lanes per 64-byte row; rows past the buffer read as zero.  Scales: this
-  // wave loads the words of A rows 64 wave .. +63 and of B rows 64 wave ..
-  // +63 (lane l: row .. + l) of slab kt / 2.
+  // lanes per 64-byte row; rows past the buffer read as zero.  Scales, 16
+  // bytes per lane from 16-byte aligned addresses (the dword form of the
+  // LDS-direct load costs about as much per instruction and needs four
+  // times as many): counting words from the scale pointer rounded down to
+  // 16 bytes, the words of tile rows 0.. of slab q start at word w(q); the
+  // stage receives the 512 words from w(q) & ~3 on (waves 0 and 1: A; 2 and
+  // 3: B), so tile row m sits at word m + (w(q) & 3) of its block.  For B,
+  // w(q) & 3 is the same for every q (N and n0 are multiples of 32 and 256).
   const int r_row_l = lane >> 2;
   const int r_chunk = mx_swz(r_row_l, lane & 3);
   const u32x4 ra = make_rsrc_words(A + (size_t)row0 * Kd, (long long)(a_rows - row0) * Kd);
@@ -380,17 +392,19 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   const uint32_t b_off = (uint32_t)((r_row_l + 16 * wave) * kMxBK + r_chunk * 16);
   const uint32_t d_off = (uint32_t)((r_row_l + 16 * wave) * Kd + r_chunk * 16);
   const uint32_t d_stride = (uint32_t)(4 * 16 * Kd);
-  const u32x4 rsa = make_rsrc_words(As, (long long)nslab * a_ld * 4);
-  const u32x4 rsb = make_rsrc_words(Bs + (size_t)seg * nslab * N * 4, (long long)nslab * N * 4);
-  const uint32_t sa_off = (uint32_t)(row0 + 64 * wave + lane) * 4;
-  const uint32_t sb_off = (uint32_t)(n0 + 64 * wave + lane) * 4;
-  const uint32_t sa_slab = (uint32_t)a_ld * 4, sb_slab = (uint32_t)N * 4;
+  const int a_mis = (int)(((uintptr_t)As & 15) >> 2);
+  const uint8_t* bs_seg = Bs + (size_t)seg * nslab * N * 4;
+  const int b_mis = (int)(((uintptr_t)bs_seg & 15) >> 2);
+  const u32x4 rsa = make_rsrc_words(As - 4 * a_mis, ((long long)nslab * a_ld + a_mis) * 4);
+  const u32x4 rsb = make_rsrc_words(bs_seg - 4 * b_mis, ((long long)nslab * N + b_mis) * 4);
+  auto a_word0 = [&](int q) { return a_mis + q * a_ld + row0; };  // w(q) of A
+  auto b_word0 = [&](int q) { return b_mis + q * N + n0; };       // w(q) of B
 
   auto stage_addr = [&](int kt) {
-    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt & (kMxStages - 1)) * kMxStageBytes);
+    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kt & (kMxStages - 1)) * kMx4StageBytes);
   };
-  // load d of step kt: 0-3 A, 4-7 B, 8 and 9 the A and B scale words (even
-  // steps only)
+  // load d of step kt: 0-3 A, 4-7 B, 8 this wave's scale words (even steps,
+  // waves 0-2)
   auto dma = [&](uint32_t st, int d, int kt) {
     const bool in_k = kt * kMxBK < Kd;
     if (d < kMxW4Dma) {
@@ -400,22 +414,17 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       const int e = d - kMxW4Dma;
       dma_load16(st + kMxBM * kMxBK + (4 * e + wave) * 1024,
                  in_k ? b_off + e * (4 * 16 * kMxBK) + (uint32_t)kt * (kMxBN * kMxBK) : kOob, rb);
-    } else if (d == 2 * kMxW4Dma) {
-      dma_load4(st + kMxDataBytes + wave * 256,
-                in_k ? sa_off + (uint32_t)(kt >> 1) * sa_slab : kOob, rsa);
     } else {
-      dma_load4(st + kMxDataBytes + 1024 + wave * 256,
-                in_k ? sb_off + (uint32_t)(kt >> 1) * sb_slab : kOob, rsb);
+      const int w = wave < 2 ? a_word0(kt >> 1) : b_word0(kt >> 1);
+      const uint32_t off = ((uint32_t)(w & ~3) + 256u * (wave & 1) + 4u * lane) * 4;
+      dma_load16(st + kMx4AScale + wave * 1024, in_k ? off : kOob, wave < 2 ? rsa : rsb);
     }
   };
   auto issue_step = [&](int kt) {
     const uint32_t st = stage_addr(kt);
 #pragma unroll
     for (int d = 0; d < 2 * kMxW4Dma; ++d) dma(st, d, kt);
-    if ((kt & 1) == 0) {
-      dma(st, 2 * kMxW4Dma, kt);
-      dma(st, 2 * kMxW4Dma + 1, kt);
-    }
+    if ((kt & 1) == 0) dma(st, 2 * kMxW4Dma, kt);
   };
 
   // ---- LDS -> register fragments: tile i of the wave's rows is rows
@@ -425,8 +434,8 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   const uint32_t a_rd1 = (uint32_t)ra_row * kMxBK + (uint32_t)mx_swz(ra_row, kh + 2) * 16;
   const uint32_t b_rd0 = kMxBM * kMxBK + (uint32_t)rb_row * kMxBK + (uint32_t)mx_swz(rb_row, kh) * 16;
   const uint32_t b_rd1 = kMxBM * kMxBK + (uint32_t)rb_row * kMxBK + (uint32_t)mx_swz(rb_row, kh + 2) * 16;
-  const uint32_t sa_rd = kMxDataBytes + (uint32_t)ra_row * 4;
-  const uint32_t sb_rd = kMxDataBytes + 1024 + (uint32_t)rb_row * 4;
+  const uint32_t sa_rd = kMx4AScale + (uint32_t)ra_row * 4;  // + 4 sh(q)
+  const uint32_t sb_rd = kMx4BScale + (uint32_t)(rb_row + (b_mis + n0) % 4) * 4;
   auto read_a = [&](uint32_t st, int i) {
     return frag(lds_b128(st + a_rd0 + i * 32 * kMxBK), lds_b128(st + a_rd1 + i * 32 * kMxBK));
   };
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
                   i32x8* nb) {
     constexpr int P = decltype(par)::value;  // kt & 1
     // younger than step kt+1: steps kt+2 and kt+3 (one of them even)
-    wait_vmcnt<4 * kMxW4Dma + 2>();
+    wait_vmcnt<4 * kMxW4Dma + 1>();
     wait_lgkm0();  // this wave's reads of slot kt % 4 (refilled below) are done
     block_barrier();
 
@@ -453,9 +462,10 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
     const uint32_t st1 = stage_addr(kt + 1);
     const uint32_t stf = stage_addr(kt + kMxStages);
     if (P == 1) {  // step kt+1 starts a pair: its scale words, early
+      const uint32_t sh = (uint32_t)(a_word0((kt + 1) >> 1) & 3) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        wa[i] = lds_b32(st1 + sa_rd + i * 128);
+        wa[i] = lds_b32(st1 + sa_rd + sh + i * 128);
         wb[i] = lds_b32(st1 + sb_rd + i * 128);
       }
     }
@@ -486,10 +496,7 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       }
       dma(stf, kMxW4Dma + i, kt + kMxStages);
     }
-    if (P == 0) {
-      dma(stf, 2 * kMxW4Dma, kt + kMxStages);  // step kt+4 is even
-      dma(stf, 2 * kMxW4Dma + 1, kt + kMxStages);
-    }
+    if (P == 0) dma(stf, 2 * kMxW4Dma, kt + kMxStages);  // step kt+4 is even
   };
   using kTrue = std::integral_constant<bool, true>;
   using kFalse = std::integral_constant<bool, false>;
@@ -503,14 +510,14 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   issue_step(1);
   issue_step(2);
   issue_step(3);
-  wait_vmcnt<6 * kMxW4Dma + 2>();  // step 0 landed: younger are steps 1, 2 (+2), 3
+  wait_vmcnt<6 * kMxW4Dma + 1>();  // step 0 landed: younger are steps 1-3 (+1 scale load)
   block_barrier();
   i32x8 pa[4], pb[4], qa[4], qb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pa[i] = read_a(lds0, i);
     pb[i] = read_b(lds0, i);
-    wa[i] = lds_b32(lds0 + sa_rd + i * 128);
+    wa[i] = lds_b32(lds0 + sa_rd + (uint32_t)(a_word0(0) & 3) * 4 + i * 128);
     wb[i] = lds_b32(lds0 + sb_rd + i * 128);
   }
   step(P0{}, kTrue{}, 0, pa, pb, qa, qb);
@@ -575,7 +582,7 @@ static hipError_t launch_mx8(const MxGemmArgs& a, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (MOE_MX8_W4)
-    k_grouped_gemm_mx8w4<EPI><<<(unsigned)grid, kMxW4Threads, kMxSmem, st>>>(
+    k_grouped_gemm_mx8w4<EPI><<<(unsigned)grid, kMxW4Threads, kMx4Smem, st>>>(
         a.A, a.As, a.B, a.Bs, a.C, a.Cs, a.offsets, a.G, a.fixed_rows,
         a.offsets ? a.max_rows : a.fixed_rows, a.a_ld, a.c_ld, mtb, a.Kd, a.N, xcd_chunk_for(ntc));
   else

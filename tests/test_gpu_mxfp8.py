@@ -323,6 +323,47 @@ def test_determinism_bitwise():
     assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
 
 
+def _offset_copy(t, off):
+    """A copy of byte tensor t that starts `off` bytes past a 16-byte boundary."""
+    big = torch.zeros(t.numel() + 32, dtype=torch.uint8, device=t.device)
+    base = (-big.data_ptr()) % 16
+    v = big[base + off:base + off + t.numel()]
+    v.copy_(t.reshape(-1))
+    return v.view(t.shape)
+
+
+@pytest.mark.parametrize("off", [4, 8, 12])
+def test_misaligned_scale_pointers_bitwise(off):
+    """Scale pointers need only 4-byte alignment: the GEMM loads the scale
+    words of a tile from the pointer rounded down to 16 bytes and shifts its
+    reads.  Every scale tensor of moe_expert_ffn_mxfp8 (inputs, weights and
+    the h / shared-expert h it writes and reads back) moved `off` bytes off
+    16-byte alignment gives bitwise the same codes and scales."""
+    import dataclasses
+    w = Workload("mis", T=600, H=256, E=8, K=2, h=192, hs=128, cf=1.25)
+    p = make_inputs(w, seed=23, device="cuda")
+    buf, mw = run_mx(w, p)
+    print(f"[misaligned scales off={off}] {w}", flush=True)
+    outs = ("h_q", "h_s", "out_q", "out_s", "hsh_q", "hsh_s", "sh_q", "sh_s")
+    # reference: the aligned call again, into zeroed outputs (bytes the GEMMs
+    # never write then compare equal)
+    ref = dataclasses.replace(buf, **{n: torch.zeros_like(getattr(buf, n)) for n in outs})
+    layer.expert_ffn_mxfp8(ref, mw)
+    mb = dataclasses.replace(
+        buf, **{n: _offset_copy(getattr(buf, n), off) for n in ("xp_s", "x_s")},
+        **{n: torch.zeros_like(getattr(buf, n)) for n in ("h_q", "out_q", "hsh_q", "sh_q")},
+        **{n: _offset_copy(torch.zeros_like(getattr(buf, n)), off)
+           for n in ("h_s", "out_s", "hsh_s", "sh_s")})
+    mm = dataclasses.replace(
+        mw, **{n: _offset_copy(getattr(mw, n), off) for n in ("w1_s", "w2_s", "ws1_s", "ws2_s")})
+    for t in (mb.xp_s, mb.h_s, mm.w1_s, mm.w2_s):
+        assert t.data_ptr() % 16 == off
+    layer.expert_ffn_mxfp8(mb, mm)
+    torch.cuda.synchronize()
+    for name in outs:
+        assert torch.equal(getattr(ref, name), getattr(mb, name)), name
+
+
 # ---------------------------------------------------------------- full size
 
 def test_mixtral_full_size_sampled():
