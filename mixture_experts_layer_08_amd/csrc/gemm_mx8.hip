@@ -330,10 +330,16 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
 // refills are for step kt+4 into slot kt % 4 itself, whose fragments every
 // wave read during step kt-1: three steps of latency cover for each load.
 // The scale words of a step pair are read early in the step before the pair
-// and their bytes extracted at the start of each step.
+// and their bytes extracted at the start of each step.  The two row-waves
+// take the tile's 32-row groups in turn, and a wave whose groups hold no
+// valid rows (a segment's last tile) skips their MFMAs, A fragment reads
+// and A loads: the loop is instantiated for 0 to 4 active groups.  (With
+// contiguous rows per wave, one SIMD of a short last tile would keep all of
+// its work, as the bf16 four-wave kernel showed.)
 //
 // Measured against the eight-wave kernel (mixtral-sized MXFP8 forward, A/B
-// on one box): 6.41 vs 6.47 ms for both GEMMs, at a higher clock (1.9 vs
+// on one box, before the row-group skipping, which took another 1.2%):
+// 6.41 vs 6.47 ms for both GEMMs, at a higher clock (1.9 vs
 // 1.7-1.8 GHz: less LDS traffic) but fewer MFMA-busy cycles (57-63% vs
 // 60-70%).  Counter runs of the earlier forms: two loads back to back per
 // group of four MFMAs, 6.74 ms; spread as above, 6.58 ms; the refill
@@ -408,8 +414,9 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   auto dma = [&](uint32_t st, int d, int kt) {
     const bool in_k = kt * kMxBK < Kd;
     if (d < kMxW4Dma) {
+      const bool live = in_k && 16 * (4 * d + wave) + r_row_l < rows;  // rows past the tile: zeros
       dma_load16(st + (4 * d + wave) * 1024,
-                 in_k ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
+                 live ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
     } else if (d < 2 * kMxW4Dma) {
       const int e = d - kMxW4Dma;
       dma_load16(st + kMxBM * kMxBK + (4 * e + wave) * 1024,
@@ -427,9 +434,12 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
     if ((kt & 1) == 0) dma(st, 2 * kMxW4Dma, kt);
   };
 
-  // ---- LDS -> register fragments: tile i of the wave's rows is rows
-  // wm 128 + 32 i + rr (+ 2 KiB per i), chunks kh and kh + 2 ----
-  const int ra_row = wm * 128 + rr, rb_row = wn * 128 + rr;
+  // ---- LDS -> register fragments: row tile i of the wave is rows
+  // (2 i + wm) 32 + rr (+ 4 KiB per i; the two row-waves take the tile's 32-row
+  // groups in turn, so that a segment's last tile, whose valid rows are a
+  // prefix, leaves both about the same number of groups), chunks kh and
+  // kh + 2; column tile j is columns wn 128 + 32 j + rr ----
+  const int ra_row = wm * 32 + rr, rb_row = wn * 128 + rr;
   const uint32_t a_rd0 = (uint32_t)ra_row * kMxBK + (uint32_t)mx_swz(ra_row, kh) * 16;
   const uint32_t a_rd1 = (uint32_t)ra_row * kMxBK + (uint32_t)mx_swz(ra_row, kh + 2) * 16;
   const uint32_t b_rd0 = kMxBM * kMxBK + (uint32_t)rb_row * kMxBK + (uint32_t)mx_swz(rb_row, kh) * 16;
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   const uint32_t sa_rd = kMx4AScale + (uint32_t)ra_row * 4;  // + 4 sh(q)
   const uint32_t sb_rd = kMx4BScale + (uint32_t)(rb_row + (b_mis + n0) % 4) * 4;
   auto read_a = [&](uint32_t st, int i) {
-    return frag(lds_b128(st + a_rd0 + i * 32 * kMxBK), lds_b128(st + a_rd1 + i * 32 * kMxBK));
+    return frag(lds_b128(st + a_rd0 + i * 64 * kMxBK), lds_b128(st + a_rd1 + i * 64 * kMxBK));
   };
   auto read_b = [&](uint32_t st, int j) {
     return frag(lds_b128(st + b_rd0 + j * 32 * kMxBK), lds_b128(st + b_rd1 + j * 32 * kMxBK));
@@ -445,8 +455,11 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
 
   f32x16 acc[4][4];  // set by the first step's MFMAs (zero C operand)
   uint32_t wa[4], wb[4];
-  auto step = [&](auto par, auto first_c, int kt, const i32x8* ca, const i32x8* cb, i32x8* na,
-                  i32x8* nb) {
+  // One K-step with the MFMAs of the first NT row tiles (the rest hold no
+  // valid rows of this tile).
+  auto step = [&](auto nt_c, auto par, auto first_c, int kt, const i32x8* ca, const i32x8* cb,
+                  i32x8* na, i32x8* nb) {
+    constexpr int NT = decltype(nt_c)::value;
     constexpr int P = decltype(par)::value;  // kt & 1
     // younger than step kt+1: steps kt+2 and kt+3 (one of them even)
     wait_vmcnt<4 * kMxW4Dma + 1>();
@@ -465,21 +478,25 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       const uint32_t sh = (uint32_t)(a_word0((kt + 1) >> 1) & 3) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        wa[i] = lds_b32(st1 + sa_rd + sh + i * 128);
+        wa[i] = lds_b32(st1 + sa_rd + sh + i * 256);
         wb[i] = lds_b32(st1 + sb_rd + i * 128);
       }
     }
     auto mm = [&](int i, int j) {
-      if (decltype(first_c)::value)
+      if (i >= NT) {
+        // defined on every path (the epilogue skips these tiles)
+        if (decltype(first_c)::value) acc[i][j] = f32x16{};
+      } else if (decltype(first_c)::value) {
         acc[i][j] = mfma_mx8(cb[j], ca[i], f32x16{}, sb[j], sa[i]);
-      else
+      } else {
         acc[i][j] = mfma_mx8(cb[j], ca[i], acc[i][j], sb[j], sa[i]);
+      }
     };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mm(i, 0);
       mm(i, 1);
-      na[i] = read_a(st1, i);
+      if (i < NT) na[i] = read_a(st1, i);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -512,27 +529,38 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   issue_step(3);
   wait_vmcnt<6 * kMxW4Dma + 1>();  // step 0 landed: younger are steps 1-3 (+1 scale load)
   block_barrier();
-  i32x8 pa[4], pb[4], qa[4], qb[4];
+  auto k_loop = [&](auto nt_c) {
+    constexpr int NT = decltype(nt_c)::value;
+    i32x8 pa[4], pb[4], qa[4], qb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pa[i] = read_a(lds0, i);
-    pb[i] = read_b(lds0, i);
-    wa[i] = lds_b32(lds0 + sa_rd + (uint32_t)(a_word0(0) & 3) * 4 + i * 128);
-    wb[i] = lds_b32(lds0 + sb_rd + i * 128);
-  }
-  step(P0{}, kTrue{}, 0, pa, pb, qa, qb);
-  int kt = 1;
-  for (; kt + 1 < KT; kt += 2) {
-    step(P1{}, kFalse{}, kt, qa, qb, pa, pb);
-    step(P0{}, kFalse{}, kt + 1, pa, pb, qa, qb);
-  }
-  if (kt < KT) step(P1{}, kFalse{}, kt, qa, qb, pa, pb);
+    for (int i = 0; i < 4; ++i) {
+      if (i < NT) pa[i] = read_a(lds0, i);
+      pb[i] = read_b(lds0, i);
+      wa[i] = lds_b32(lds0 + sa_rd + (uint32_t)(a_word0(0) & 3) * 4 + i * 256);
+      wb[i] = lds_b32(lds0 + sb_rd + i * 128);
+    }
+    step(nt_c, P0{}, kTrue{}, 0, pa, pb, qa, qb);
+    int kt = 1;
+    for (; kt + 1 < KT; kt += 2) {
+      step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb);
+      step(nt_c, P0{}, kFalse{}, kt + 1, pa, pb, qa, qb);
+    }
+    if (kt < KT) step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb);
+  };
+  // row tiles of this wave that hold valid rows: tile i starts at row (2 i + wm) 32
+  const int nt_rows = __builtin_amdgcn_readfirstlane(min(max((rows - 32 * wm + 63) >> 6, 0), 4));
+  if (nt_rows == 4) k_loop(std::integral_constant<int, 4>{});
+  else if (nt_rows == 3) k_loop(std::integral_constant<int, 3>{});
+  else if (nt_rows == 2) k_loop(std::integral_constant<int, 2>{});
+  else if (nt_rows == 1) k_loop(std::integral_constant<int, 1>{});
+  else k_loop(std::integral_constant<int, 0>{});
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 
   // ---- epilogue, per 32 x 32 tile as in the eight-wave kernel ----
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = wm * 128 + i * 32 + rr;
+    if (i >= nt_rows) continue;  // no valid rows (uniform)
+    const int m = (2 * i + wm) * 32 + rr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int nb = n0 + wn * 128 + j * 32;  // first column of this tile's block

@@ -277,6 +277,11 @@ CASES = [
     ("T1", dict(T=1, H=64, E=4, K=2, h=64, cf=1.25)),
     ("E256_K8", dict(T=130, H=64, E=256, K=8, h=64, cf=1.25)),
     ("C1_drops", dict(T=257, H=64, E=8, K=2, h=64, cf=0.01)),
+    # one segment whose last 256-row tile holds 33, 161 and 224 rows: the two
+    # row-waves of the GEMM own 1/1, 3/3 and 4/3 of its 32-row groups
+    ("tail_33", dict(T=289, H=128, E=1, K=1, h=128, cf=0.0)),
+    ("tail_161", dict(T=417, H=128, E=1, K=1, h=128, cf=0.0)),
+    ("tail_224", dict(T=480, H=128, E=1, K=1, h=128, cf=0.0)),
 ]
 
 
