@@ -799,16 +799,12 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     bf16* crow = (bf16*)Cv + (size_t)(row0 + m) * N;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      u32x2 d[2];
+      u32x2 d[2], us[2];  // output and (train-mode GELU) pre-activation groups
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = 2 * p + h;
         float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-        const int c = n0 + cbase_e + 16 * j + 4 * lg_e;  // this lane's 4 columns
-        const bool ok = c < N;                           // whole group of 4 in or out
-        const size_t at = (size_t)(row0 + m) * N + c;
-        if (EPI == kEpiGeluSave && ok)
-          *(u32x2*)(Ep + at) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        if (EPI == kEpiGeluSave) us[h] = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         if (EPI == kEpiGelu || EPI == kEpiGeluSave) {
           v0 = gelu_tanh_f32(v0);
           v1 = gelu_tanh_f32(v1);
@@ -835,6 +831,13 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
       const u32x4 o = odd ? u32x4{x0, x1, d[1][0], d[1][1]} : u32x4{d[0][0], d[0][1], x0, x1};
       const int c0 = n0 + cbase_e + 16 * (2 * p + (odd ? 1 : 0)) + 4 * (lg_e & ~1);
       if (c0 < N) *(u32x4*)(crow + c0) = o;
+      if (EPI == kEpiGeluSave) {  // the pre-activations, paired the same way
+        const u32x2 su = odd ? us[0] : us[1];
+        const uint32_t y0 = (uint32_t)__shfl_xor((int)su[0], 16, kWave);
+        const uint32_t y1 = (uint32_t)__shfl_xor((int)su[1], 16, kWave);
+        const u32x4 ou = odd ? u32x4{y0, y1, us[1][0], us[1][1]} : u32x4{us[0][0], us[0][1], y0, y1};
+        if (c0 < N) *(u32x4*)(Ep + (size_t)(row0 + m) * N + c0) = ou;
+      }
     }
   }
 }
