@@ -255,6 +255,51 @@ def router_noise_leg(w, p, dev, steps: int) -> dict:
             "note": "moe_route (router GEMM, noise, softmax, top-k, block histograms)"}
 
 
+def mfma_ceiling_leg(dev, gemm_tflops: float, peak: float, runs: int = 5) -> dict:
+    """The MFMA-only rate of the grouped GEMM's inner loop (moe_mfma_ceiling):
+    one workgroup of four waves per CU (one wave per SIMD, as the four-wave
+    GEMM kernel), 64 v_mfma_f32_16x16x32_bf16 per round on random operands
+    held in registers, no memory traffic.  Under this load the chip holds a
+    clock below the 2.4 GHz the nominal peak assumes, so the rate is the
+    practical ceiling the GEMM's rate is read against.  Also timed: two
+    alternating operand sets (every sign and mantissa bit switching between
+    rounds) and a zero-word XOR of every operand per round (one VALU
+    instruction per MFMA).  Median of `runs` each."""
+    import torch
+
+    from mixture_experts_layer_08_amd import binding as B
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(7)
+    ops = torch.randn((16, 64, 8), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((cus * 256 * 4,), dtype=torch.float32, device=dev)
+    iters = 20000
+    flop = 2.0 * 16 * 16 * 32 * 64 * iters * 4 * cus
+    stream = torch.cuda.current_stream()
+
+    def median_ms(mode: int) -> float:
+        B.moe_mfma_ceiling(ops, out, cus, iters // 10, mode, stream)  # warm-up
+        times = []
+        for _ in range(runs):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            B.moe_mfma_ceiling(ops, out, cus, iters, mode, stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]))
+        return sorted(times)[len(times) // 2]
+
+    ms, ms_alt, ms_xor = median_ms(0), median_ms(1), median_ms(2)
+    tf, tf_alt, tf_xor = (flop / (t * 1e-3) / 1e12 for t in (ms, ms_alt, ms_xor))
+    return {"tflops": tf, "frac_of_peak": tf / peak, "ms": ms,
+            "tflops_alternating_sets": tf_alt, "tflops_one_valu_per_mfma": tf_xor,
+            "iters": iters, "workgroups": cus, "gemm_frac_of_ceiling": gemm_tflops / tf,
+            "note": "MFMA-only loop of the four-wave GEMM's shape on random register operands "
+                    "(moe_mfma_ceiling mode 0); tflops_alternating_sets: mode 1, every sign and "
+                    "mantissa bit switching between rounds; tflops_one_valu_per_mfma: mode 2; "
+                    "gemm_frac_of_ceiling = roofline.achieved / tflops"}
+
+
 def dense_ffn_ratio(w, p, dev, fwd_ms: float, steps: int) -> dict:
     """The pages' single-GPU sanity check: the MoE forward's time over that of
     one dense FFN of the same T, H, h (expert 0's weights) run through the
@@ -562,6 +607,8 @@ def main():
         "hbm": hbm,
         "cpu_baseline": None,
     }
+    if w.dtype == "bf16":
+        res["mfma_ceiling"] = mfma_ceiling_leg(dev, gm["achieved"], gm["peak"])
     if not a.no_side_legs:
         res["router_noise"] = router_noise_leg(w, p, dev, 20)
         res["dense_ffn_sanity"] = dense_ffn_ratio(w, p, dev, ms_step, 10)

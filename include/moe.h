@@ -468,6 +468,33 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
                                 void* stream);
 
 /*
+ * moe_mfma_ceiling - a measurement aid, not a step of the layer: the
+ * MFMA-only rate of the grouped GEMM's inner loop, the ceiling its roofline
+ * fraction is read against.  `workgroups` workgroups of four waves (one wave
+ * per SIMD when there is one workgroup per CU) each run `iters` rounds
+ * t = 0 .. iters-1 of 64 v_mfma_f32_16x16x32_bf16 (8 x 8 tiles, 256 fp32
+ * accumulators per lane) on operands held in registers, with no memory
+ * traffic in the loop: 2 * 16 * 16 * 32 * 64 * iters FLOP per wave.
+ *   mode 0    the given operands in every round
+ *   mode 1    two register sets alternate: the given operands in even
+ *             rounds, in odd rounds those with every bf16 sign and mantissa
+ *             bit flipped (each 32-bit word XORed with 0x807f807f)
+ *   mode 2    the given operands, each XORed before every round with a zero
+ *             word passed in at run time (one VALU instruction per MFMA,
+ *             results as mode 0)
+ *   operands  16 x 64 x 8 bf16, 16-byte aligned: fragments 0-7 are A_0..A_7,
+ *             8-15 are B_0..B_7; lane l of a fragment holds row l % 16,
+ *             k = 8 (l / 16) .. +7 of a 16 x 32 matrix
+ *   out       workgroups * 256 * 4 floats, 16-byte aligned: lane l of a wave
+ *             writes rows 4 (l / 16) + r (r = 0..3), column l % 16 of
+ *             sum over the rounds t of sum_{i,j} B_j(t) A_i(t)^T
+ * MOE_ERR_INVALID_ARG for null or misaligned pointers, workgroups outside
+ * [1, 65536], iters outside [1, 2^24] or mode other than 0, 1 or 2.
+ */
+moe_status moe_mfma_ceiling(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                            int32_t mode, void* stream);
+
+/*
  * moe_forward_noalloc - the whole forward (moe_route, moe_aux_loss,
  * moe_permute, moe_expert_ffn, moe_combine, in that order, on `stream`) in
  * one call that allocates nothing, for callers that cannot allocate: code

@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_expert_ffn_backward", "moe_permute_backward", "moe_mx_operand_scale_bytes",
     "moe_mx_weight_code_bytes",
     "moe_quantize_weights_mxfp8", "moe_permute_mxfp8", "moe_expert_ffn_mxfp8",
-    "moe_combine_mxfp8", "moe_forward_noalloc",
+    "moe_combine_mxfp8", "moe_forward_noalloc", "moe_mfma_ceiling",
 )
 
 
@@ -127,6 +127,8 @@ def lib():
         L.moe_combine_mxfp8.argtypes = [_SHAPE, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_forward_noalloc.argtypes = [_SHAPE] + [_P] * 23 + [_P]
+        L.moe_mfma_ceiling.restype = ctypes.c_int
+        L.moe_mfma_ceiling.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
         _lib = L
     return _lib
 
@@ -290,3 +292,8 @@ def moe_forward_noalloc(s, x, w_router, b_router, w1, w2, ws1, ws2, logits, topk
         _ptr(counts), _ptr(kept), _ptr(offsets), _ptr(row_of), _ptr(token_of),
         _ptr(n_dropped), _ptr(xp), _ptr(hbuf), _ptr(out), _ptr(hshared), _ptr(shared_out),
         _ptr(y), _stream(stream)))
+
+
+def moe_mfma_ceiling(operands, out, workgroups: int, iters: int, mode: int = 0, stream=None):
+    _check("moe_mfma_ceiling", lib().moe_mfma_ceiling(
+        _ptr(operands), _ptr(out), int(workgroups), int(iters), int(mode), _stream(stream)))

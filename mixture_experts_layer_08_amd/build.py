@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_mx8.hip", "mxfp8.hip", "combine.hip",
-           "backward.hip", "api.hip"]
+           "backward.hip", "ceiling.hip", "api.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

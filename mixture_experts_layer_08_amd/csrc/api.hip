@@ -288,6 +288,16 @@ moe_status moe_count_nonfinite(const moe_shape* s, const float* logits, int64_t*
                                            (long long*)count, (hipStream_t)stream));
 }
 
+moe_status moe_mfma_ceiling(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                            int32_t mode, void* stream) {
+  if (!operands || !out || !aligned16(operands) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+  if (workgroups < 1 || workgroups > (1 << 16) || iters < 1 || iters > (1 << 24) ||
+      mode < 0 || mode > 2)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_mfma_ceiling(operands, out, workgroups, iters, mode, (hipStream_t)stream));
+}
+
 moe_status moe_aux_loss(const moe_shape* s, const void* ws, size_t ws_bytes, float* aux,
                         void* stream) {
   moe_status st = moe_check_shape(s);

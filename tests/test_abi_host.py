@@ -167,6 +167,18 @@ def _call_route(lib, s, ws_ptr=0x1000, ws_bytes=1 << 30, ptr=0x2000):
     return lib.moe_route(ctypes.byref(s), ptr, ptr, None, ptr, ptr, ptr, ws_ptr, ws_bytes, None)
 
 
+def test_mfma_ceiling_rejects_bad_arguments(lib):
+    """The MFMA-only measurement kernel: null or misaligned pointers and sizes
+    out of range are refused before any launch."""
+    assert lib.moe_mfma_ceiling(None, 0x2000, 1, 1, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2004, 1, 1, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 0, 1, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 0, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1 << 17, 1, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 1, 3, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 1, -1, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_count_nonfinite_rejects_bad_arguments(lib):
     assert lib.moe_count_nonfinite(ctypes.byref(shape()), None, 0x2000, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_count_nonfinite(ctypes.byref(shape()), 0x2000, None, None) == B.MOE_ERR_INVALID_ARG
