@@ -481,10 +481,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // hide their own latencies, which the schedule below does.
 //
 // Stage layout and LDS-direct loads as in the eight-wave kernel (4-stage
-// ring, 32 KiB stages), except the "cols" form's chunk swizzle: chunk c of k
-// row k is stored at c ^ (4 (k & 3) + 2 ((k >> 3) & 1)).  The fragment of k
+// ring, 32 KiB stages), except the chunk swizzles.  "cols" form: chunk c of k
+// row k is stored at c ^ (4 (k & 3) + 2 ((k >> 3) & 1)); the fragment of k
 // rows 8g .. 8g+7 that lane group g reads by transposing reads would
-// otherwise put the rows k and k + 8 of one read on the same banks.
+// otherwise put the rows k and k + 8 of one read on the same banks.  "rows"
+// form: chunk c of row m is stored at c ^ ((m >> 1) & 3).  A 16-byte read
+// serves 8 consecutive lanes per pass, here rows m .. m+7 of one k chunk:
+// rows m and m + 2 share their 128-byte bank window (64-byte rows), so the
+// key must differ between them.  The eight-wave kernel's key (m >> 2) & 3
+// does not, and costs these reads a 2-way conflict on every pass (measured
+// with SQ_LDS_BANK_CONFLICT: half of the LDS cycles of a read).
 //
 // Per K-step: wait until step kt+1 has landed for every wave (s_waitcnt on
 // the own loads, then the barrier), then 64 MFMAs on fragments read during
@@ -504,8 +510,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // (their A rows are not fetched either).  A tile with at most 128 valid
 // columns (row-major forms) uses 4 x 1 waves of 64 x 128 instead of 2 x 2 of
 // 128 x 128, so no wave multiplies only zeros.
+//
+// Address arithmetic in the loop.  With one wave per SIMD, every vector ALU
+// instruction besides the MFMAs takes an issue slot from the MFMA stream (an
+// MFMA-only loop loses 18% of its MFMA-busy cycles to one independent VALU
+// instruction per MFMA).  When the contraction is a multiple of BK2 and A is
+// in "rows" form (row-major and transposed-weight forms), no load crosses the
+// contraction's end: each lane's load offsets are then fixed for the tile
+// (those of invalid rows or columns already past num_records) and the K-step
+// advance rides in the buffer instruction's scalar offset, and the "rows"
+// fragment reads of a pair of steps share one per-lane base (slots 2q and
+// 2q + 1, the second at an immediate +kStageBytes) made by an opaque add, so
+// that the reads differ by immediate offsets only.  Per two K-steps that
+// leaves 17 VALU instructions beside the 128 MFMAs instead of 76 (the
+// transposing reads' XOR-swizzled addresses still take one add each; giving
+// them per-pair bases as well was 1.8% slower).  Measured A/B on one box:
+// expert FFN 12.13 -> 11.67 ms at T=32768 H=4096 E=8 top-2 h=14336, its
+// backward 25.2 -> 24.9 ms, outputs bitwise equal.
 constexpr int kW4Threads = 256;
 constexpr int kW4Dma = 4;  // LDS-direct loads per operand, per wave, per stage
+__device__ __forceinline__ int w4_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv, bf16* Ep,
@@ -557,7 +581,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // (k >> 3) & 1 = d & 1; k rows past the contraction range lie beyond
   // num_records, and columns past the operand's width are not fetched.
   const int r_row_l = lane >> 2;
-  const int r_chunk = a_swz(r_row_l, lane & 3);
+  const int r_chunk = w4_swz(r_row_l, lane & 3);  // (row >> 1) & 3 is d- and wave-invariant
   const int c_row0 = (lane >> 5) + 2 * wave;
   const int c_chunk0 = (lane & 31) ^ (4 * (c_row0 & 3)), c_chunk1 = c_chunk0 ^ 2;
   // A
@@ -603,6 +627,26 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     b_live0 = n0 + c_chunk0 * 8 < N;
     b_live1 = n0 + c_chunk1 * 8 < N;
   }
+  // Fixed-offset loads (contraction a multiple of BK2, not the TN form): a
+  // lane's offsets, invalid ones already past num_records, and the K-step
+  // advance as the scalar offset.  Either reading of the range check (with
+  // or without the scalar offset) gives the same result: a valid offset plus
+  // the advance stays inside the operand.
+  const bool kfast = !kTN && Kd % BK2 == 0;
+  uint32_t av[kW4Dma], bv[kW4Dma];
+#pragma unroll
+  for (int d = 0; d < kW4Dma; ++d) {
+    av[d] = a_live[d] ? ((d & 1) ? a_off1 : a_off0) + d * a_dstride : kOob;
+    bv[d] = (kBRows || ((d & 1) ? b_live1 : b_live0)) ? ((d & 1) ? b_off1 : b_off0) + d * b_dstride
+                                                      : kOob;
+  }
+  auto dma_fast = [&](uint32_t st, int d, int kt) {
+    if (d < kW4Dma)
+      dma_load16_s(st + (4 * d + wave) * 1024, av[d], (uint32_t)kt * a_kstride, ra_src);
+    else
+      dma_load16_s(st + BM2 * BK2 * 2 + (4 * (d - kW4Dma) + wave) * 1024, bv[d - kW4Dma],
+                   (uint32_t)kt * b_kstride, rb_src);
+  };
   auto dma = [&](uint32_t st, int d, int kt) {
     if (d < kW4Dma) {
       const uint32_t off = ((d & 1) ? a_off1 : a_off0) + d * a_dstride + (uint32_t)kt * a_kstride;
@@ -640,7 +684,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // transposing reads give lane column li, k 8 lg .. +7); with the swizzle,
   // the 32-byte column step f becomes an XOR with 32 (f ^ (2 (li / 4) +
   // lg % 2)).
-  auto rows_rd = [&](int r0) { return (uint32_t)(r0 + li) * 64 + 16 * (lg ^ ((li >> 2) & 3)); };
+  auto rows_rd = [&](int r0) { return (uint32_t)(r0 + li) * 64 + 16 * w4_swz(li, lg); };
   auto cols_rd = [&](int c0) {
     return (uint32_t)(8 * lg + (li >> 2)) * 512 + 16 * (c0 / 8 + ((li >> 1) & 1)) + 8 * (li & 1) +
            32 * (2 * (li >> 2) + (lg & 1));
@@ -668,8 +712,18 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // One K-step with the MFMAs of the first NG groups.  The first step's
   // accumulators start from a zero C operand, so that the compiler never
   // materialises 256 zeros in ordinary registers.
-  auto step = [&](auto ng_c, auto first_c, auto afs_c, int kt, const bf16x8* ca,
-                  const bf16x8* cb, bf16x8* na, bf16x8* nb) {
+  // The per-lane address of a "rows" fragment read, stage slot included,
+  // made once per pair of steps by an opaque add (a pair reads slots 2q and
+  // 2q + 1, the second at +kStageBytes): the reads then differ only by
+  // immediate offsets, where the compiler would otherwise keep 8 hoisted
+  // per-fragment addresses and add the stage base to each.
+  auto rows_base = [&](uint32_t st, uint32_t rd) {
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(st), "v"(rd));
+    return r;
+  };
+  auto step = [&](auto ng_c, auto first_c, auto afs_c, auto fast_c, int kt, const bf16x8* ca,
+                  const bf16x8* cb, bf16x8* na, bf16x8* nb, uint32_t ra, uint32_t rb) {
     constexpr int NG = decltype(ng_c)::value;
     constexpr uint32_t AFS = decltype(afs_c)::value;  // A fragment stride (rows form)
     wait_vmcnt<(kDist - 1) * 2 * kW4Dma>();  // younger than step kt+1: kDist - 1 steps
@@ -687,9 +741,17 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      na[i] = frag(kARows, st1, a_rd, AFS, i);
-      nb[i] = frag(kBRows, st1, b_rd, 1024, i);
-      dma(stf, i, kt + kDist + 1);
+      if (decltype(fast_c)::value) {
+        na[i] = lds_read_b128(ra + i * AFS);  // A is in "rows" form here
+        nb[i] = kBRows ? lds_read_b128(rb + i * 1024) : frag(false, st1, b_rd, 1024, i);
+      } else {
+        na[i] = frag(kARows, st1, a_rd, AFS, i);
+        nb[i] = frag(kBRows, st1, b_rd, 1024, i);
+      }
+      if (decltype(fast_c)::value)
+        dma_fast(stf, i, kt + kDist + 1);
+      else
+        dma(stf, i, kt + kDist + 1);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -703,45 +765,63 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   const int KT = (k_end - k_begin + BK2 - 1) / BK2;
   // These vmcnt counts hold only while the LDS-direct loads are the loop's
   // only vector-memory instructions: the build refuses a spill.
-#pragma unroll
-  for (int s = 0; s <= kDist; ++s) {
-    const uint32_t st = stage_addr(s);
-#pragma unroll
-    for (int d = 0; d < 2 * kW4Dma; ++d) dma(st, d, s);
-  }
-  wait_vmcnt<kDist * 2 * kW4Dma>();  // step 0 landed (own loads)
-  block_barrier();                             // ... and every wave's
-  auto k_loop = [&](auto ng_c, auto afs_c) {
+  auto k_loop = [&](auto ng_c, auto afs_c, auto fast_c) {
     constexpr uint32_t AFS = decltype(afs_c)::value;
+#pragma unroll
+    for (int s = 0; s <= kDist; ++s) {
+      const uint32_t st = stage_addr(s);
+#pragma unroll
+      for (int d = 0; d < 2 * kW4Dma; ++d) {
+        if (decltype(fast_c)::value)
+          dma_fast(st, d, s);
+        else
+          dma(st, d, s);
+      }
+    }
+    wait_vmcnt<kDist * 2 * kW4Dma>();  // step 0 landed (own loads)
+    block_barrier();                   // ... and every wave's
     bf16x8 pa[8], pb[8], qa[8], qb[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       pa[f] = frag(kARows, lds0, a_rd, AFS, f);
       pb[f] = frag(kBRows, lds0, b_rd, 1024, f);
     }
-    step(ng_c, kTrue{}, afs_c, 0, pa, pb, qa, qb);
+    constexpr bool F = decltype(fast_c)::value;
+    {
+      const uint32_t st = stage_addr(1);
+      const uint32_t ra = F ? rows_base(st, a_rd) : 0u, rb = F && kBRows ? rows_base(st, b_rd) : 0u;
+      step(ng_c, kTrue{}, afs_c, fast_c, 0, pa, pb, qa, qb, ra, rb);
+    }
     int kt = 1;
     for (; kt + 1 < KT; kt += 2) {
-      step(ng_c, kFalse{}, afs_c, kt, qa, qb, pa, pb);
-      step(ng_c, kFalse{}, afs_c, kt + 1, pa, pb, qa, qb);
+      const uint32_t st = stage_addr(kt + 1);  // slot 2 or 0; the pair's second step reads the next
+      const uint32_t ra = F ? rows_base(st, a_rd) : 0u, rb = F && kBRows ? rows_base(st, b_rd) : 0u;
+      step(ng_c, kFalse{}, afs_c, fast_c, kt, qa, qb, pa, pb, ra, rb);
+      step(ng_c, kFalse{}, afs_c, fast_c, kt + 1, pa, pb, qa, qb, ra + kStageBytes,
+           rb + kStageBytes);
     }
-    if (kt < KT) step(ng_c, kFalse{}, afs_c, kt, qa, qb, pa, pb);
+    if (kt < KT) {
+      const uint32_t st = stage_addr(kt + 1);
+      const uint32_t ra = F ? rows_base(st, a_rd) : 0u, rb = F && kBRows ? rows_base(st, b_rd) : 0u;
+      step(ng_c, kFalse{}, afs_c, fast_c, kt, qa, qb, pa, pb, ra, rb);
+    }
   };
   // a segment's last tile, and the narrow layout, run fewer groups
   using Inter = std::integral_constant<uint32_t, 32 * 64>;
   using Contig = std::integral_constant<uint32_t, 16 * 64>;
-  if (inter) {
-    if (ng == 8) k_loop(std::integral_constant<int, 8>{}, Inter{});
-    else if (ng == 6) k_loop(std::integral_constant<int, 6>{}, Inter{});
-    else if (ng == 4) k_loop(std::integral_constant<int, 4>{}, Inter{});
-    else if (ng == 2) k_loop(std::integral_constant<int, 2>{}, Inter{});
-    else k_loop(std::integral_constant<int, 0>{}, Inter{});
+  auto by_ng = [&](auto afs_c, auto fast_c) {
+    if (ng == 8) k_loop(std::integral_constant<int, 8>{}, afs_c, fast_c);
+    else if (ng == 6) k_loop(std::integral_constant<int, 6>{}, afs_c, fast_c);
+    else if (ng == 4) k_loop(std::integral_constant<int, 4>{}, afs_c, fast_c);
+    else if (ng == 2) k_loop(std::integral_constant<int, 2>{}, afs_c, fast_c);
+    else k_loop(std::integral_constant<int, 0>{}, afs_c, fast_c);
+  };
+  if (kfast) {
+    if (inter) by_ng(Inter{}, kTrue{});
+    else by_ng(Contig{}, kTrue{});
   } else {
-    if (ng == 8) k_loop(std::integral_constant<int, 8>{}, Contig{});
-    else if (ng == 6) k_loop(std::integral_constant<int, 6>{}, Contig{});
-    else if (ng == 4) k_loop(std::integral_constant<int, 4>{}, Contig{});
-    else if (ng == 2) k_loop(std::integral_constant<int, 2>{}, Contig{});
-    else k_loop(std::integral_constant<int, 0>{}, Contig{});
+    if (inter) by_ng(Inter{}, kFalse{});
+    else by_ng(Contig{}, kFalse{});
   }
   wait_vmcnt<0>();  // drain the loads issued past the end before the grid exits
 

@@ -121,6 +121,18 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
                : "memory", "m0");
 }
 
+// dma_load16 with the buffer's scalar offset as well: the 16 bytes at
+// voff + soff (soff wave-uniform).  A loop that advances every lane's
+// offset by the same amount each step passes that advance here, with no
+// per-lane add.
+__device__ __forceinline__ void dma_load16_s(uint32_t lds_addr, uint32_t voff, uint32_t soff,
+                                             u32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // 4 bytes per lane from buffer offset `voff` straight into LDS at
 // lds_addr + 4 * lane (the dword form of dma_load16).
 __device__ __forceinline__ void dma_load4(uint32_t lds_addr, uint32_t voff, u32x4 rsrc) {

@@ -169,7 +169,9 @@ def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz:
             "k_grouped_gemm_w4 (GEMM2)": r"k_grouped_gemm_w4<\s*0\s*,\s*0>",
             "k_grouped_gemm_mx8w4 (GEMM1, GELU)": r"k_grouped_gemm_mx8w4<1>",
             "k_grouped_gemm_mx8w4 (GEMM2)": r"k_grouped_gemm_mx8w4<0>",
-            "k_mfma_ceiling (MFMA only, no memory)": r"k_mfma_ceiling",
+            "k_mfma_ceiling<0> (MFMA only, no memory)": r"k_mfma_ceiling<0>",
+            "k_mfma_ceiling<1> (two alternating operand sets)": r"k_mfma_ceiling<1>",
+            "k_mfma_ceiling<2> (one VALU instruction per MFMA)": r"k_mfma_ceiling<2>",
             "k_permute (memory-bound)": r"k_permute<",
             "k_combine (memory-bound)": r"k_combine<"}
     per = collections.defaultdict(dict)
