@@ -19,7 +19,10 @@
 // 4 x 2 v_mfma_scale_f32_32x32x64_f8f6f4 tiles; one K-step is 64 values = 64
 // bytes per row, so a stage holds the same
 // 32 KiB (A [256][64 B], B [256][64 B], 16-byte chunk c of row r stored at
-// c ^ ((r >> 2) & 3)), filled by LDS-direct loads through a 4-stage ring.
+// c ^ ((r >> 1) & 3): a 16-byte read serves 8 consecutive lanes, i.e. 8
+// consecutive rows, per pass, and rows r and r + 2 share a 128-byte bank
+// window, so the key must tell them apart), filled by LDS-direct loads
+// through a 4-stage ring.
 // The block scales ride in the same ring: every even step's stage also
 // carries one 4-byte word per A row and per B row (the scales of that step
 // and the next), loaded by one LDS-direct dword load per wave.
@@ -63,7 +66,7 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
 __device__ __forceinline__ uint32_t lds_b32(uint32_t addr) { return *(const lds_u32*)(uintptr_t)addr; }
-__device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
 __device__ __forceinline__ i32x8 frag(u32x4 lo, u32x4 hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -345,6 +348,14 @@ __global__ __launch_bounds__(kMxThreads, 1) void k_grouped_gemm_mx8(
 // group of four MFMAs, 6.74 ms; spread as above, 6.58 ms; the refill
 // distance of two steps left the waves waiting 21% of their cycles, three
 // steps 17%.
+//
+// As in the bf16 four-wave kernel, the loop keeps vector ALU work off the
+// MFMA stream: the data loads' per-lane offsets are fixed for the tile with
+// the K-step advance in the scalar offset, and the fragment and scale-word
+// reads of each pair of steps share per-lane bases made once per pair.  Per
+// two K-steps 25 VALU instructions instead of 95 (-0.4% for both GEMMs of
+// the MXFP8 forward, A/B on one box, outputs bitwise equal: the 64-cycle
+// MFMAs leave more room for them than the bf16 kernel's 16-cycle ones).
 constexpr int kMxW4Threads = 256;
 constexpr int kMxW4Dma = 4;  // data LDS-direct loads per operand, per wave, per stage
 
@@ -411,16 +422,25 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
   };
   // load d of step kt: 0-3 A, 4-7 B, 8 this wave's scale words (even steps,
   // waves 0-2)
+  // Data loads: a lane's offsets are fixed for the tile (rows past the
+  // tile's valid rows already past num_records) and the K-step advance is
+  // the scalar offset, clamped to the last step for the refills issued past
+  // the end (never read), so that every load stays inside its operand.
+  const int kt_last = Kd / kMxBK - 1;  // the launcher requires Kd a positive multiple of kMxBK
+  uint32_t av[kMxW4Dma], bv[kMxW4Dma];
+#pragma unroll
+  for (int d = 0; d < kMxW4Dma; ++d) {
+    av[d] = 16 * (4 * d + wave) + r_row_l < rows ? d_off + d * d_stride : kOob;
+    bv[d] = b_off + d * (4 * 16 * kMxBK);
+  }
   auto dma = [&](uint32_t st, int d, int kt) {
     const bool in_k = kt * kMxBK < Kd;
+    const uint32_t kc = (uint32_t)min(kt, kt_last);
     if (d < kMxW4Dma) {
-      const bool live = in_k && 16 * (4 * d + wave) + r_row_l < rows;  // rows past the tile: zeros
-      dma_load16(st + (4 * d + wave) * 1024,
-                 live ? d_off + d * d_stride + (uint32_t)kt * kMxBK : kOob, ra);
+      dma_load16_s(st + (4 * d + wave) * 1024, av[d], kc * kMxBK, ra);
     } else if (d < 2 * kMxW4Dma) {
       const int e = d - kMxW4Dma;
-      dma_load16(st + kMxBM * kMxBK + (4 * e + wave) * 1024,
-                 in_k ? b_off + e * (4 * 16 * kMxBK) + (uint32_t)kt * (kMxBN * kMxBK) : kOob, rb);
+      dma_load16_s(st + kMxBM * kMxBK + (4 * e + wave) * 1024, bv[e], kc * (kMxBN * kMxBK), rb);
     } else {
       const int w = wave < 2 ? a_word0(kt >> 1) : b_word0(kt >> 1);
       const uint32_t off = ((uint32_t)(w & ~3) + 256u * (wave & 1) + 4u * lane) * 4;
@@ -455,10 +475,28 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
 
   f32x16 acc[4][4];  // set by the first step's MFMAs (zero C operand)
   uint32_t wa[4], wb[4];
+  // Per-lane read addresses with the stage slot included, made once per pair
+  // of steps by an opaque add (a pair reads slots 2q and 2q + 1, the second
+  // at +kMx4StageBytes), so that the reads differ by immediate offsets only.
+  auto obase = [&](uint32_t st, uint32_t rd) {
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(st), "v"(rd));
+    return r;
+  };
+  struct Bases {
+    uint32_t a0, a1, b0, b1, sa, sb;
+  };
+  auto bases = [&](int kt_read) {  // kt_read: the first step of the pair whose slots are read
+    const uint32_t st = stage_addr(kt_read);
+    const uint32_t sh = (uint32_t)(a_word0(kt_read >> 1) & 3) * 4;
+    return Bases{obase(st, a_rd0), obase(st, a_rd1), obase(st, b_rd0),
+                 obase(st, b_rd1), obase(st, sa_rd + sh), obase(st, sb_rd)};
+  };
   // One K-step with the MFMAs of the first NT row tiles (the rest hold no
-  // valid rows of this tile).
+  // valid rows of this tile).  bs: the bases of the slot this step reads
+  // (slot kt + 1), boff: 0 or kMx4StageBytes.
   auto step = [&](auto nt_c, auto par, auto first_c, int kt, const i32x8* ca, const i32x8* cb,
-                  i32x8* na, i32x8* nb) {
+                  i32x8* na, i32x8* nb, const Bases& bs, uint32_t boff) {
     constexpr int NT = decltype(nt_c)::value;
     constexpr int P = decltype(par)::value;  // kt & 1
     // younger than step kt+1: steps kt+2 and kt+3 (one of them even)
@@ -472,14 +510,12 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       sa[i] = (int)((wa[i] >> (8 * (2 * P + kh))) & 0xffu);
       sb[i] = (int)((wb[i] >> (8 * (2 * P + kh))) & 0xffu);
     }
-    const uint32_t st1 = stage_addr(kt + 1);
     const uint32_t stf = stage_addr(kt + kMxStages);
     if (P == 1) {  // step kt+1 starts a pair: its scale words, early
-      const uint32_t sh = (uint32_t)(a_word0((kt + 1) >> 1) & 3) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        wa[i] = lds_b32(st1 + sa_rd + sh + i * 256);
-        wb[i] = lds_b32(st1 + sb_rd + i * 128);
+        wa[i] = lds_b32(bs.sa + boff + i * 256);
+        wb[i] = lds_b32(bs.sb + boff + i * 128);
       }
     }
     auto mm = [&](int i, int j) {
@@ -496,7 +532,8 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
     for (int i = 0; i < 4; ++i) {
       mm(i, 0);
       mm(i, 1);
-      if (i < NT) na[i] = read_a(st1, i);
+      if (i < NT)
+        na[i] = frag(lds_b128(bs.a0 + boff + i * 64 * kMxBK), lds_b128(bs.a1 + boff + i * 64 * kMxBK));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -505,7 +542,7 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       dma(stf, i, kt + kMxStages);
       mm(i, 2);
       mm(i, 3);
-      nb[i] = read_b(st1, i);
+      nb[i] = frag(lds_b128(bs.b0 + boff + i * 32 * kMxBK), lds_b128(bs.b1 + boff + i * 32 * kMxBK));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -539,13 +576,20 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
       wa[i] = lds_b32(lds0 + sa_rd + (uint32_t)(a_word0(0) & 3) * 4 + i * 256);
       wb[i] = lds_b32(lds0 + sb_rd + i * 128);
     }
-    step(nt_c, P0{}, kTrue{}, 0, pa, pb, qa, qb);
+    {
+      const Bases b1 = bases(1);  // step 0 reads slot 1 (its scale words are not read: P = 0)
+      step(nt_c, P0{}, kTrue{}, 0, pa, pb, qa, qb, b1, 0u);
+    }
     int kt = 1;
     for (; kt + 1 < KT; kt += 2) {
-      step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb);
-      step(nt_c, P0{}, kFalse{}, kt + 1, pa, pb, qa, qb);
+      const Bases b = bases(kt + 1);  // slots 2q and 2q + 1
+      step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb, b, 0u);
+      step(nt_c, P0{}, kFalse{}, kt + 1, pa, pb, qa, qb, b, kMx4StageBytes);
     }
-    if (kt < KT) step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb);
+    if (kt < KT) {
+      const Bases b = bases(kt + 1);
+      step(nt_c, P1{}, kFalse{}, kt, qa, qb, pa, pb, b, 0u);
+    }
   };
   // row tiles of this wave that hold valid rows: tile i starts at row (2 i + wm) 32
   const int nt_rows = __builtin_amdgcn_readfirstlane(min(max((rows - 32 * wm + 63) >> 6, 0), 4));
