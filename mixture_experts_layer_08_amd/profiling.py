@@ -228,7 +228,7 @@ def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16",
     matching dispatches in dispatch order (e.g. the timed forward's launches
     of a run that also has other legs); None takes every matching one."""
     rows = list(csv.DictReader(open(stats_csv)))
-    short = lambda n: re.sub(r"\(.*", "", n).replace("void ", "")[:70]
+    short = lambda n: re.sub(r"\(.*", "", n.replace("(anonymous namespace)::", "")).replace("void ", "")[:70]
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```",
              cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |",
