@@ -219,6 +219,75 @@ def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz:
     print("\n".join(lines))
 
 
+SQ_KERNELS = {"k_grouped_gemm_w4 (GEMM1, GELU)": r"k_grouped_gemm_w4<\s*0\s*,\s*1>",
+              "k_grouped_gemm_w4 (GEMM2)": r"k_grouped_gemm_w4<\s*0\s*,\s*0>",
+              "k_mfma_ceiling<0> (MFMA only)": r"k_mfma_ceiling<0>",
+              "k_mfma_ceiling<1> (alternating operand sets)": r"k_mfma_ceiling<1>",
+              "k_mfma_ceiling<2> (one VALU instruction per MFMA)": r"k_mfma_ceiling<2>"}
+
+
+def sq(csv_paths, title, cmd, out, xcds: int = 8, simds: int = 1024):
+    """Markdown table of the grouped GEMM's instruction mix, waits and LDS
+    conflicts beside the MFMA-only kernel's, from several `--pmc` passes of
+    the same command (one csv per pass; counters summed over a dispatch's
+    dimensions, averaged over a kernel's dispatches after the first):
+      - clock = GRBM_GUI_ACTIVE / XCDs / duration; MFMA busy per cycle =
+        SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / (clock x duration);
+      - instructions per MFMA: SQ_INSTS_VALU counts the MFMAs too, so the
+        other VALU instructions are SQ_INSTS_VALU - SQ_INSTS_MFMA;
+      - waits per wave-cycle: SQ_WAIT_ANY and SQ_WAIT_INST_ANY over
+        SQ_WAVE_CYCLES (all three in quad-cycles);
+      - LDS bank-conflict share: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    acc = {n: collections.defaultdict(list) for n in SQ_KERNELS}
+    for path in csv_paths:
+        per = collections.defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            v = per[int(r["Dispatch_Id"])]
+            v["name"] = r["Kernel_Name"]
+            v["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        seen = collections.Counter()
+        for d in sorted(per):
+            v = per[d]
+            for n, rx in SQ_KERNELS.items():
+                if re.search(rx, v["name"]):
+                    seen[n] += 1
+                    if seen[n] > 1:  # the first dispatch of each kernel is a warm-up
+                        for c, x in v.items():
+                            if c != "name":
+                                acc[n][c].append(x)
+                    break
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X; one run per "
+             "counter set):", "", "```", cmd, "```", "",
+             "Counters summed over each dispatch's dimensions and averaged over a kernel's "
+             "dispatches after the first.  Clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy "
+             "= SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (clock x duration); SQ_INSTS_VALU counts "
+             "MFMAs too, so other VALU = SQ_INSTS_VALU - SQ_INSTS_MFMA; waits over SQ_WAVE_CYCLES "
+             "(quad-cycles, as the waits); LDS conflict share = SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel | clock GHz | MFMA busy | other VALU / MFMA | SALU / MFMA | LDS instr / MFMA "
+             "| SQ_WAIT_ANY / wave-cycle | SQ_WAIT_INST_ANY / wave-cycle | LDS conflict share |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for n in SQ_KERNELS:
+        m = {c: mean(xs) for c, xs in acc[n].items()}
+        if not m:
+            continue
+        dur = m["dur"]
+        ghz = m["GRBM_GUI_ACTIVE"] / xcds / dur / 1e9
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / (ghz * 1e9 * dur)
+        mf = m["SQ_INSTS_MFMA"]
+        act = m["SQ_LDS_IDX_ACTIVE"]
+        lines.append(
+            f"| `{n}` | {ghz:.2f} | {busy:.1%} | {(m['SQ_INSTS_VALU'] - mf) / mf:.2f} | "
+            f"{m['SQ_INSTS_SALU'] / mf:.2f} | {m['SQ_INSTS_LDS'] / mf:.2f} | "
+            f"{m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1%} | "
+            f"{m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1%} | "
+            + (f"{m['SQ_LDS_BANK_CONFLICT'] / act:.1%} |" if act else "- |"))
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats(stats_csv, trace_csv, bench_log, title, cmd, note, out, kernel="bf16", top=14,
           window=None):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run: the kernel
@@ -298,6 +367,11 @@ def main():
     st.add_argument("--window", default=None, metavar="START:COUNT",
                     help="only these matching dispatches, in dispatch order")
     st.add_argument("--out", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("--csv", nargs="+", required=True, help="counter_collection.csv of each pass")
+    q.add_argument("--title", required=True)
+    q.add_argument("--command", required=True, help="the commands that produced the passes")
+    q.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "traffic":
         traffic(a.fetch, a.write, a.copy_bytes, a.workload, a.out, a.kernel)
@@ -307,6 +381,8 @@ def main():
         win = tuple(int(v) for v in a.window.split(":")) if a.window else None
         stats(a.stats, a.trace, a.bench_log, a.title, a.command, a.note, a.out, a.kernel,
               window=win)
+    elif a.cmd == "sq":
+        sq(a.csv, a.title, a.command, a.out)
     else:
         clock(a.csv, a.title, a.command, a.out)
 
