@@ -112,13 +112,16 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, long long byt
 // lds_addr + 16 * lane (wave-uniform lds_addr).  Issued as inline asm so the
 // compiler does not treat it as an LDS store that every later LDS read must
 // wait for: the ring's explicit vmcnt waits and barriers order it instead.
+// The LDS address is the asm's m0 operand, so that the compiler writes m0
+// itself, straight from the address arithmetic (one s_add_i32 m0, ... per
+// load rather than an add and a move).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // dma_load16 with the buffer's scalar offset as well: the 16 bytes at
@@ -127,19 +130,19 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
 // per-lane add.
 __device__ __forceinline__ void dma_load16_s(uint32_t lds_addr, uint32_t voff, uint32_t soff,
                                              u32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // 4 bytes per lane from buffer offset `voff` straight into LDS at
 // lds_addr + 4 * lane (the dword form of dma_load16).
 __device__ __forceinline__ void dma_load4(uint32_t lds_addr, uint32_t voff, u32x4 rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
 }
 #pragma clang diagnostic pop
 
