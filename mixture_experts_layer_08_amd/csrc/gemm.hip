@@ -42,14 +42,12 @@ namespace moe {
 // a stage's loads is an explicit vmcnt.
 //
 // LDS stage (32 KiB): A [256 m][32 k] (64-byte rows, 16-byte chunk c stored
-// at c ^ ((m >> 1) & 3)) then B [32 k][256 n] (512-byte rows, 16-byte chunk c
+// at c ^ ((m >> 2) & 3)) then B [32 k][256 n] (512-byte rows, 16-byte chunk c
 // stored at c ^ (4 * (k & 3))).  Each LDS-direct instruction of a wave fills
 // 1 KiB in lane order; a lane fetches the global chunk that the swizzle maps
-// to its slot.  Both swizzles make the fragment reads below conflict-free: a
-// 16-byte read serves 8 consecutive lanes per pass, here rows m .. m+7 of one
-// k chunk, and rows m and m + 2 share their 128-byte bank window (64-byte
-// rows), so the key must tell them apart (the key (m >> 2) & 3 does not and
-// gave these reads a 2-way conflict, measured with SQ_LDS_BANK_CONFLICT).
+// to its slot.  Both swizzles make the fragment reads below conflict-free
+// (measured with SQ_LDS_BANK_CONFLICT on the read pattern alone: the 32
+// lanes of a half-wave read 32 consecutive rows of one k chunk).
 //
 // The MFMA runs with the operands swapped (B^T fragment as "A"), so each lane
 // accumulates C^T: per 32x32 tile it owns row m = lane%32 and columns
@@ -61,7 +59,7 @@ constexpr int BM2 = 256, BN2 = 256, BK2 = 32;
 constexpr int kGemmThreads = 512;
 constexpr int kSub = BK2 / 16;  // MFMA k-substeps per K-step
 constexpr int kDma = 2;         // LDS-direct loads per operand, per wave, per stage
-__device__ __forceinline__ int a_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int a_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 4
 #endif
@@ -168,7 +166,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
   // "rows" form: instruction d of this wave covers stage rows 16*(8d + wave)
   // .. +15, four lanes per 64-byte row; a k chunk past Kd reads as zero.
   const int r_row_l = lane >> 2;
-  const int r_chunk = a_swz(r_row_l, lane & 3);  // (row >> 1) & 3 is d- and wave-invariant
+  const int r_chunk = a_swz(r_row_l, lane & 3);  // (row >> 2) & 3 is d- and wave-invariant
   // "cols" form: instruction d covers k rows 2*(8d + wave) .. +1, 32 lanes per
   // 512-byte row; k rows past the contraction range lie beyond num_records.
   const int c_row0 = (lane >> 5) + 2 * wave;     // (row & 3) is d-invariant
@@ -485,10 +483,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // hide their own latencies, which the schedule below does.
 //
 // Stage layout and LDS-direct loads as in the eight-wave kernel (4-stage
-// ring, 32 KiB stages), except the "cols" form's chunk swizzle: chunk c of k
-// row k is stored at c ^ (4 (k & 3) + 2 ((k >> 3) & 1)).  The fragment of k
+// ring, 32 KiB stages), except the chunk swizzles.  "cols" form: chunk c of k
+// row k is stored at c ^ (4 (k & 3) + 2 ((k >> 3) & 1)); the fragment of k
 // rows 8g .. 8g+7 that lane group g reads by transposing reads would
-// otherwise put the rows k and k + 8 of one read on the same banks.
+// otherwise put the rows k and k + 8 of one read on the same banks.  "rows"
+// form: chunk c of row m at c ^ ((m >> 1) & 3).  Here the 16 lanes of a
+// quarter-wave read 16 consecutive rows of one k chunk, and the eight-wave
+// kernel's key (m >> 2) & 3 gave every such read a 2-way conflict (a third of
+// the LDS's busy cycles, SQ_LDS_BANK_CONFLICT); this key gives none.  Each
+// key was chosen by measuring the read pattern alone: the eight-wave and
+// MXFP8 reads (32 rows per chunk) conflict with this key and not with theirs.
 //
 // Per K-step: wait until step kt+1 has landed for every wave (s_waitcnt on
 // the own loads, then the barrier), then 64 MFMAs on fragments read during
@@ -527,6 +531,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // backward 25.2 -> 24.9 ms, outputs bitwise equal.
 constexpr int kW4Threads = 256;
 constexpr int kW4Dma = 4;  // LDS-direct loads per operand, per wave, per stage
+__device__ __forceinline__ int w4_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv, bf16* Ep,
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // (k >> 3) & 1 = d & 1; k rows past the contraction range lie beyond
   // num_records, and columns past the operand's width are not fetched.
   const int r_row_l = lane >> 2;
-  const int r_chunk = a_swz(r_row_l, lane & 3);  // (row >> 1) & 3 is d- and wave-invariant
+  const int r_chunk = w4_swz(r_row_l, lane & 3);  // (row >> 1) & 3 is d- and wave-invariant
   const int c_row0 = (lane >> 5) + 2 * wave;
   const int c_chunk0 = (lane & 31) ^ (4 * (c_row0 & 3)), c_chunk1 = c_chunk0 ^ 2;
   // A
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   // transposing reads give lane column li, k 8 lg .. +7); with the swizzle,
   // the 32-byte column step f becomes an XOR with 32 (f ^ (2 (li / 4) +
   // lg % 2)).
-  auto rows_rd = [&](int r0) { return (uint32_t)(r0 + li) * 64 + 16 * a_swz(li, lg); };
+  auto rows_rd = [&](int r0) { return (uint32_t)(r0 + li) * 64 + 16 * w4_swz(li, lg); };
   auto cols_rd = [&](int c0) {
     return (uint32_t)(8 * lg + (li >> 2)) * 512 + 16 * (c0 / 8 + ((li >> 1) & 1)) + 8 * (li & 1) +
            32 * (2 * (li >> 2) + (lg & 1));

@@ -19,10 +19,12 @@
 // 4 x 2 v_mfma_scale_f32_32x32x64_f8f6f4 tiles; one K-step is 64 values = 64
 // bytes per row, so a stage holds the same
 // 32 KiB (A [256][64 B], B [256][64 B], 16-byte chunk c of row r stored at
-// c ^ ((r >> 1) & 3): a 16-byte read serves 8 consecutive lanes, i.e. 8
-// consecutive rows, per pass, and rows r and r + 2 share a 128-byte bank
-// window, so the key must tell them apart), filled by LDS-direct loads
-// through a 4-stage ring.
+// c ^ ((r >> 2) & 3)), filled by LDS-direct loads through a 4-stage ring.
+// The key is the measured conflict-free one for this kernel's reads, in
+// which the 32 lanes of each half-wave read 32 consecutive rows of one k
+// chunk (SQ_LDS_BANK_CONFLICT on each read pattern alone: zero with this
+// key, a 2-way conflict on every read with (r >> 1) & 3, the key the bf16
+// four-wave kernel's reads of 16 rows per chunk need).
 // The block scales ride in the same ring: every even step's stage also
 // carries one 4-byte word per A row and per B row (the scales of that step
 // and the next), loaded by one LDS-direct dword load per wave.
@@ -66,7 +68,7 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
 __device__ __forceinline__ uint32_t lds_b32(uint32_t addr) { return *(const lds_u32*)(uintptr_t)addr; }
-__device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 __device__ __forceinline__ i32x8 frag(u32x4 lo, u32x4 hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
