@@ -475,12 +475,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // block as 8 x 8 v_mfma_f32_16x16x32_bf16 tiles (256 fp32 accumulators per
 // lane, in AGPRs).  Same layouts and epilogues as the eight-wave kernel.
 //
-// Why a second kernel: the grouped GEMM is power-limited (the eight-wave
-// kernel runs its MFMAs ~75% of its cycles at ~1.5 GHz).  With one wave per
-// SIMD and 128 x 128 per wave, a K-step reads 64 KiB of fragments from LDS
-// per CU instead of 96, and the 16 x 16 MFMA draws less power per FLOP than
-// the 32 x 32 one, so the clock holds ~1.9 GHz; the four waves must then
-// hide their own latencies, which the schedule below does.
+// Why a second kernel: the eight-wave kernel runs its MFMAs ~75% of its
+// cycles at only ~1.5 GHz.  With one wave per SIMD and 128 x 128 per wave, a
+// K-step reads 64 KiB of fragments from LDS per CU instead of 96, and the
+// clock holds ~1.7-1.8 GHz (an MFMA-only loop of this shape holds ~2.0); the
+// four waves must then hide their own latencies, which the schedule below
+// does.
 //
 // Stage layout and LDS-direct loads as in the eight-wave kernel (4-stage
 // ring, 32 KiB stages), except the chunk swizzles.  "cols" form: chunk c of k
@@ -513,10 +513,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // columns (row-major forms) uses 4 x 1 waves of 64 x 128 instead of 2 x 2 of
 // 128 x 128, so no wave multiplies only zeros.
 //
-// Address arithmetic in the loop.  With one wave per SIMD, every vector ALU
-// instruction besides the MFMAs takes an issue slot from the MFMA stream (an
-// MFMA-only loop loses 18% of its MFMA-busy cycles to one independent VALU
-// instruction per MFMA).  When the contraction is a multiple of BK2 and A is
+// Address arithmetic in the loop.  With one wave per SIMD, every instruction
+// besides the MFMAs takes an issue slot of the wave that the MFMA stream
+// competes for (an MFMA-only loop of this shape loses 11-12% of its rate to
+// one independent VALU instruction per MFMA, issued in a group per round).  When the contraction is a multiple of BK2 and A is
 // in "rows" form (row-major and transposed-weight forms), no load crosses the
 // contraction's end: each lane's load offsets are then fixed for the tile
 // (those of invalid rows or columns already past num_records) and the K-step

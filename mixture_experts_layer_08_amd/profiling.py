@@ -45,11 +45,21 @@ KERNELS = {
 COPY_KERNEL = "copyBuffer"  # the HIP runtime's device-to-device copy kernel
 
 
+def code_of(text: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed:
+    an edit to a comment leaves it, and so a recorded profile, unchanged.
+    (No string literal in these sources holds a comment marker.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_source_hash(kernel: str = "bf16") -> str:
-    """Hash of a grouped GEMM's sources (the kernel and its shared helpers)."""
+    """Hash of the code of a grouped GEMM's sources (the kernel and its shared
+    helpers), comments left out."""
     h = hashlib.sha256()
     for name in KERNELS[kernel][1]:
-        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
+        h.update(code_of(open(os.path.join(PKG, "csrc", name)).read()).encode())
     return h.hexdigest()[:16]
 
 
