@@ -29,3 +29,15 @@ def test_shared_expert_is_one_more_segment():
     with_sh = counters.segment_roofline_s([10, 20], H, h, b, P, BW, shared_rows=30, hs=hs)
     sh = counters.segment_roofline_s([30], H, hs, b, P, BW)
     assert all(x == pytest.approx(y + z) for x, y, z in zip(with_sh, base, sh))
+
+
+def test_profile_hash_ignores_comments_not_code():
+    """A recorded profile stays valid across comment edits of the GEMM
+    sources and is dropped for any change to their code."""
+    from mixture_experts_layer_08_amd.profiling import code_of
+
+    base = "int f(int a) {\n  // step\n  return a + 1; /* one */\n}\n"
+    assert code_of(base) == code_of("int f(int a) {\n  return a + 1;   // other words\n}\n")
+    assert code_of(base) == code_of("/* header\n   lines */ int  f(int a) {\n return a + 1; }")
+    assert code_of(base) != code_of(base.replace("a + 1", "a + 2"))
+    assert code_of('asm("s_nop 0\\n\\ts_nop 0");') == 'asm("s_nop 0\\n\\ts_nop 0");'
