@@ -277,26 +277,31 @@ def mfma_ceiling_leg(dev, gemm_tflops: float, peak: float, runs: int = 5) -> dic
     flop = 2.0 * 16 * 16 * 32 * 64 * iters * 4 * cus
     stream = torch.cuda.current_stream()
 
+    out32 = torch.empty((cus * 256 * 16,), dtype=torch.float32, device=dev)  # mode 3
+
     def median_ms(mode: int) -> float:
-        B.moe_mfma_ceiling(ops, out, cus, iters // 10, mode, stream)  # warm-up
+        o = out32 if mode == 3 else out
+        B.moe_mfma_ceiling(ops, o, cus, iters // 10, mode, stream)  # warm-up
         times = []
         for _ in range(runs):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record(stream)
-            B.moe_mfma_ceiling(ops, out, cus, iters, mode, stream)
+            B.moe_mfma_ceiling(ops, o, cus, iters, mode, stream)
             ev[1].record(stream)
             torch.cuda.synchronize()
             times.append(ev[0].elapsed_time(ev[1]))
         return sorted(times)[len(times) // 2]
 
-    ms, ms_alt, ms_xor = median_ms(0), median_ms(1), median_ms(2)
-    tf, tf_alt, tf_xor = (flop / (t * 1e-3) / 1e12 for t in (ms, ms_alt, ms_xor))
+    ms, ms_alt, ms_xor, ms_32 = median_ms(0), median_ms(1), median_ms(2), median_ms(3)
+    tf, tf_alt, tf_xor, tf_32 = (flop / (t * 1e-3) / 1e12 for t in (ms, ms_alt, ms_xor, ms_32))
     return {"tflops": tf, "frac_of_peak": tf / peak, "ms": ms,
             "tflops_alternating_sets": tf_alt, "tflops_one_valu_per_mfma": tf_xor,
+            "tflops_32x32x16": tf_32,
             "iters": iters, "workgroups": cus, "gemm_frac_of_ceiling": gemm_tflops / tf,
             "note": "MFMA-only loop of the four-wave GEMM's shape on random register operands "
                     "(moe_mfma_ceiling mode 0); tflops_alternating_sets: mode 1, every sign and "
                     "mantissa bit switching between rounds; tflops_one_valu_per_mfma: mode 2; "
+                    "tflops_32x32x16: mode 3, the same work on 32x32x16 MFMAs; "
                     "gemm_frac_of_ceiling = roofline.achieved / tflops"}
 
 

@@ -482,14 +482,21 @@ moe_status moe_permute_backward(const moe_shape* s, const void* d_xp, const int3
  *   mode 2    the given operands, each XORed before every round with a zero
  *             word passed in at run time (one VALU instruction per MFMA,
  *             results as mode 0)
+ *   mode 3    the eight-wave kernel's shape instead: 4 x 4 tiles of
+ *             v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane) on
+ *             fragments 0-3 (A_0..A_3) and 8-11 (B_0..B_3) read as 32 x 16
+ *             matrices (lane l: row l % 32, k = 8 (l / 32) .. +7), each
+ *             round running its 16 MFMAs twice: the same FLOPs per round
  *   operands  16 x 64 x 8 bf16, 16-byte aligned: fragments 0-7 are A_0..A_7,
  *             8-15 are B_0..B_7; lane l of a fragment holds row l % 16,
  *             k = 8 (l / 16) .. +7 of a 16 x 32 matrix
- *   out       workgroups * 256 * 4 floats, 16-byte aligned: lane l of a wave
- *             writes rows 4 (l / 16) + r (r = 0..3), column l % 16 of
- *             sum over the rounds t of sum_{i,j} B_j(t) A_i(t)^T
+ *   out       workgroups * 256 * 4 floats (mode 3: * 16), 16-byte aligned:
+ *             lane l of a wave writes rows 4 (l / 16) + r (r = 0..3), column
+ *             l % 16 of sum over the rounds t of sum_{i,j} B_j(t) A_i(t)^T;
+ *             mode 3: rows 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15),
+ *             column l % 32 of 2 * iters * sum_{i,j} B_j A_i^T
  * MOE_ERR_INVALID_ARG for null or misaligned pointers, workgroups outside
- * [1, 65536], iters outside [1, 2^24] or mode other than 0, 1 or 2.
+ * [1, 65536], iters outside [1, 2^24] or mode other than 0, 1, 2 or 3.
  */
 moe_status moe_mfma_ceiling(const void* operands, float* out, int32_t workgroups, int32_t iters,
                             int32_t mode, void* stream);

@@ -292,7 +292,7 @@ moe_status moe_mfma_ceiling(const void* operands, float* out, int32_t workgroups
                             int32_t mode, void* stream) {
   if (!operands || !out || !aligned16(operands) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
   if (workgroups < 1 || workgroups > (1 << 16) || iters < 1 || iters > (1 << 24) ||
-      mode < 0 || mode > 2)
+      mode < 0 || mode > 3)
     return MOE_ERR_INVALID_ARG;
   return hip_status(
       launch_mfma_ceiling(operands, out, workgroups, iters, mode, (hipStream_t)stream));

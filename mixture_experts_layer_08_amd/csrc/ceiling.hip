@@ -25,9 +25,17 @@
 //   2  the given operands, XORed before every round with a zero word passed
 //      in at run time: one VALU instruction per MFMA and no bit switch, the
 //      cost of such instructions in the MFMA stream.
-// Output: each lane writes the four sums over i, j of its accumulator
-// elements, which are rows 4 (l / 16) + r, column l % 16 of
-// sum_t sum_{i,j} B_j(t) A_i(t)^T.
+//   3  the eight-wave kernel's MFMA shape instead: 4 x 4 tiles of
+//      v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane), fragments
+//      0-3 as A_0..A_3 and 8-11 as B_0..B_3 of 32 x 16 matrices (lane l:
+//      row l % 32, k = 8 (l / 32) .. +7), each round running the 16 MFMAs
+//      twice on the same operands, so that a round does the FLOPs of the
+//      other modes' rounds.
+// Output (modes 0-2): each lane writes the four sums over i, j of its
+// accumulator elements, which are rows 4 (l / 16) + r, column l % 16 of
+// sum_t sum_{i,j} B_j(t) A_i(t)^T.  Mode 3: sixteen sums per lane, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 (r = 0..15), column l % 32 of
+// 2 sum_t sum_{i,j} B_j A_i^T.
 #include "common.h"
 #include "kernels.h"
 
@@ -96,12 +104,51 @@ __global__ __launch_bounds__(256, 1) void k_mfma_ceiling(const bf16x8* __restric
   *(f32x4*)(out + ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4) = s;
 }
 
+// Mode 3: the 32 x 32 x 16 shape, 4 x 4 tiles (see the header).
+__global__ __launch_bounds__(256, 1) void k_mfma_ceiling32(const bf16x8* __restrict__ operands,
+                                                           float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    a[f] = __builtin_bit_cast(u32x4, operands[f * 64 + lane]);
+    b[f] = __builtin_bit_cast(u32x4, operands[(8 + f) * 64 + lane]);
+  }
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, b[j]), __builtin_bit_cast(bf16x8, a[i]), f32x16{}, 0, 0, 0);
+  for (int t = 0; t < 2 * iters - 1; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, b[j]), __builtin_bit_cast(bf16x8, a[i]), acc[i][j], 0, 0,
+            0);
+  }
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[i][j];
+  float* o = out + ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 16;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(f32x4*)(o + 4 * q) = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+}
+
 }  // namespace
 
 hipError_t launch_mfma_ceiling(const void* operands, float* out, int workgroups, int iters,
                                int mode, hipStream_t st) {
   const bf16x8* ops = (const bf16x8*)operands;
-  if (mode == 1)
+  if (mode == 3)
+    k_mfma_ceiling32<<<workgroups, 256, 0, st>>>(ops, out, iters);
+  else if (mode == 1)
     k_mfma_ceiling<1><<<workgroups, 256, 0, st>>>(ops, out, iters, 0u);
   else if (mode == 2)
     k_mfma_ceiling<2><<<workgroups, 256, 0, st>>>(ops, out, iters, 0u);

@@ -258,7 +258,8 @@ hipError_t launch_pad_bf16(const void* src, bool src_f32, bf16* dst, int R, int 
 // MFMA-only measurement kernel (ceiling.hip): `workgroups` workgroups of four
 // waves run `iters` rounds of 64 v_mfma_f32_16x16x32_bf16 on register
 // operands (mode 1: two register sets alternating; 2: a zero-word XOR of
-// every operand before each round); out gets 4 floats per lane.
+// every operand before each round; 3: 4 x 4 tiles of 32x32x16 MFMAs); out
+// gets 4 floats per lane (16 in mode 3).
 hipError_t launch_mfma_ceiling(const void* operands, float* out, int workgroups, int iters,
                                int mode, hipStream_t st);
 

@@ -182,6 +182,7 @@ def clock(csv_path, title, cmd, out, xcds: int = 8, simds: int = 1024, peak_ghz:
             "k_mfma_ceiling<0> (MFMA only, no memory)": r"k_mfma_ceiling<0>",
             "k_mfma_ceiling<1> (two alternating operand sets)": r"k_mfma_ceiling<1>",
             "k_mfma_ceiling<2> (one VALU instruction per MFMA)": r"k_mfma_ceiling<2>",
+            "k_mfma_ceiling32 (32x32x16 MFMAs)": r"k_mfma_ceiling32",
             "k_permute (memory-bound)": r"k_permute<",
             "k_combine (memory-bound)": r"k_combine<"}
     per = collections.defaultdict(dict)
@@ -233,7 +234,8 @@ SQ_KERNELS = {"k_grouped_gemm_w4 (GEMM1, GELU)": r"k_grouped_gemm_w4<\s*0\s*,\s*
               "k_grouped_gemm_w4 (GEMM2)": r"k_grouped_gemm_w4<\s*0\s*,\s*0>",
               "k_mfma_ceiling<0> (MFMA only)": r"k_mfma_ceiling<0>",
               "k_mfma_ceiling<1> (alternating operand sets)": r"k_mfma_ceiling<1>",
-              "k_mfma_ceiling<2> (one VALU instruction per MFMA)": r"k_mfma_ceiling<2>"}
+              "k_mfma_ceiling<2> (one VALU instruction per MFMA)": r"k_mfma_ceiling<2>",
+              "k_mfma_ceiling32 (32x32x16 MFMAs)": r"k_mfma_ceiling32"}
 
 
 def sq(csv_paths, title, cmd, out, xcds: int = 8, simds: int = 1024):

@@ -175,7 +175,7 @@ def test_mfma_ceiling_rejects_bad_arguments(lib):
     assert lib.moe_mfma_ceiling(0x2000, 0x2000, 0, 1, 0, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 0, 0, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1 << 17, 1, 0, None) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 1, 3, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 1, 4, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_ceiling(0x2000, 0x2000, 1, 1, -1, None) == B.MOE_ERR_INVALID_ARG
 
 
