@@ -516,19 +516,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // Address arithmetic in the loop.  With one wave per SIMD, every instruction
 // besides the MFMAs takes an issue slot of the wave that the MFMA stream
 // competes for (an MFMA-only loop of this shape loses 11-12% of its rate to
-// one independent VALU instruction per MFMA, issued in a group per round).  When the contraction is a multiple of BK2 and A is
-// in "rows" form (row-major and transposed-weight forms), no load crosses the
-// contraction's end: each lane's load offsets are then fixed for the tile
-// (those of invalid rows or columns already past num_records) and the K-step
-// advance rides in the buffer instruction's scalar offset, and the "rows"
-// fragment reads of a pair of steps share one per-lane base (slots 2q and
-// 2q + 1, the second at an immediate +kStageBytes) made by an opaque add, so
-// that the reads differ by immediate offsets only.  Per two K-steps that
-// leaves 17 VALU instructions beside the 128 MFMAs instead of 76 (the
-// transposing reads' XOR-swizzled addresses still take one add each; giving
-// them per-pair bases as well was 1.8% slower).  Measured A/B on one box:
-// expert FFN 12.13 -> 11.67 ms at T=32768 H=4096 E=8 top-2 h=14336, its
-// backward 25.2 -> 24.9 ms, outputs bitwise equal.
+// one independent VALU instruction per MFMA, issued in a group per round).
+// When the contraction is a multiple of BK2 and A is in "rows" form
+// (row-major and transposed-weight forms), no load crosses the contraction's
+// end: each lane's load offsets are then fixed for the tile (those of invalid
+// rows or columns already past num_records) and the K-step advance rides in
+// the buffer instruction's scalar offset, and the "rows" fragment reads of a
+// pair of steps share one per-lane base (slots 2q and 2q + 1, the second at
+// an immediate +kStageBytes) made by an opaque add, so that the reads differ
+// by immediate offsets only.  Per two K-steps that leaves 17 VALU
+// instructions beside the 128 MFMAs instead of 76 (the transposing reads'
+// XOR-swizzled addresses still take one add each; giving them per-pair bases
+// as well was 1.8% slower).  Measured A/B on one box: expert FFN 12.13 ->
+// 11.67 ms at T=32768 H=4096 E=8 top-2 h=14336, its backward 25.2 -> 24.9 ms,
+// outputs bitwise equal.
 constexpr int kW4Threads = 256;
 constexpr int kW4Dma = 4;  // LDS-direct loads per operand, per wave, per stage
 __device__ __forceinline__ int w4_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
