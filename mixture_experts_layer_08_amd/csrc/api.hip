@@ -373,31 +373,23 @@ moe_status moe_expert_ffn(const moe_shape* s, const void* xp, const int32_t* off
   const int max_rows = (int)moe_max_rows(s);
   const bool train = (s->flags & MOE_FLAG_TRAIN) != 0;
   const WsLayout L = ws_layout(s);
-  // GEMM1 (+GELU; with MOE_FLAG_TRAIN the pre-activations are kept), GEMM2.
-  // The shared expert rides along as each launch's side problem: its tiles
-  // share the routed launch's grid, so neither leaves a tail of its own.
-  GemmArgs g1 = rows_gemm(kGemmNN, train ? kEpiGeluSave : kEpiGelu, xp, w1, hbuf,
-                          train ? at<void>(ws, L.preact) : nullptr, offsets, s->E, 0, max_rows,
-                          s->H, s->h_exp);
-  GemmArgs g2 = rows_gemm(kGemmNN, kEpiStore, hbuf, w2, out, nullptr, offsets, s->E, 0, max_rows,
-                          s->h_exp, s->H);
-  if (shared) {
-    g1.side_A = x;
-    g1.side_B = ws1;
-    g1.side_C = hshared;
-    g1.side_E = train ? at<void>(ws, L.preact_sh) : nullptr;
-    g1.side_rows = s->T;
-    g1.side_Kd = s->H;
-    g1.side_N = s->h_shared;
-    g2.side_A = hshared;
-    g2.side_B = ws2;
-    g2.side_C = shared_out;
-    g2.side_rows = s->T;
-    g2.side_Kd = s->h_shared;
-    g2.side_N = s->H;
-  }
+  // GEMM1 (+GELU; with MOE_FLAG_TRAIN the pre-activations are kept), GEMM2
+  const GemmArgs g1 = rows_gemm(kGemmNN, train ? kEpiGeluSave : kEpiGelu, xp, w1, hbuf,
+                                train ? at<void>(ws, L.preact) : nullptr, offsets, s->E, 0,
+                                max_rows, s->H, s->h_exp);
+  const GemmArgs g2 = rows_gemm(kGemmNN, kEpiStore, hbuf, w2, out, nullptr, offsets, s->E, 0,
+                                max_rows, s->h_exp, s->H);
   hipError_t e = gemm(g1);
   if (e == hipSuccess) e = gemm(g2);
+  if (e == hipSuccess && shared) {
+    const GemmArgs s1 = rows_gemm(kGemmNN, train ? kEpiGeluSave : kEpiGelu, x, ws1, hshared,
+                                  train ? at<void>(ws, L.preact_sh) : nullptr, nullptr, 1, s->T,
+                                  s->T, s->H, s->h_shared);
+    const GemmArgs s2 = rows_gemm(kGemmNN, kEpiStore, hshared, ws2, shared_out, nullptr, nullptr,
+                                  1, s->T, s->T, s->h_shared, s->H);
+    e = gemm(s1);
+    if (e == hipSuccess) e = gemm(s2);
+  }
   return hip_status(e);
 }
 

@@ -530,24 +530,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm_bf16(
 // as well was 1.8% slower).  Measured A/B on one box: expert FFN 12.13 ->
 // 11.67 ms at T=32768 H=4096 E=8 top-2 h=14336, its backward 25.2 -> 24.9 ms,
 // outputs bitwise equal.
+// The epilogue's exchange between the lanes l and l ^ 16 (rows 2q and 2q + 1
+// of 16 lanes), which hold the 4-column groups g0 and g1 of one row: the lane
+// of the even row gets its own g0 and then its partner's, the lane of the odd
+// row its partner's g1 and then its own, i.e. 8 consecutive columns each.
+// v_permlane16_swap trades the odd rows of its first operand for the even
+// rows of its second, all in the VALU (no LDS round trip per exchange).
+__device__ __forceinline__ u32x4 pair_rows16(u32x2 g0, u32x2 g1) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(g0[0], g1[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(g0[1], g1[1], false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
 constexpr int kW4Threads = 256;
 constexpr int kW4Dma = 4;  // LDS-direct loads per operand, per wave, per stage
 __device__ __forceinline__ int w4_swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
-// A second, fixed-size problem of a row-major launch (the shared expert beside
-// the routed segments): its tiles are the first `tiles` workgroups of the
-// grid, in the same tile order, and the routed tiles follow.
-struct GemmSide {
-  const bf16* A;
-  const bf16* B;
-  void* C;
-  bf16* E;
-  int rows, Kd, N, tiles;
-};
 template <int LAYOUT, int EPI>
 __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
     const bf16* __restrict__ A, const bf16* __restrict__ B, void* Cv, bf16* Ep,
     const int32_t* __restrict__ offsets, int G, int fixed_rows, int a_rows, int mt_bound, int M,
-    int Kd, int N, int xcd_chunk, GemmSide side) {
+    int Kd, int N, int xcd_chunk) {
   constexpr bool kTN = LAYOUT == kGemmTN;
   constexpr bool kARows = !kTN;               // A in "rows" form
   constexpr bool kBRows = LAYOUT == kGemmNT;  // B in "rows" form
@@ -555,30 +556,12 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
   constexpr int kDist = LAYOUT == kGemmNN ? 2 : 3;
   static_assert(kDist + 1 <= kStages, "a refill needs a free slot");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  const int nt_count = (N + BN2 - 1) / BN2;
   int mt, nt, seg, row0, rows;
-  int k_begin = 0, k_end;  // contraction range; TN: the segment's packed rows
+  int k_begin = 0, k_end = Kd;  // contraction range; TN: the segment's packed rows
   {
-    int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
-    const bool on_side = !kTN && tile < side.tiles;
-    if (on_side) {
-      A = side.A;
-      B = side.B;
-      Cv = side.C;
-      Ep = side.E;
-      Kd = side.Kd;
-      N = side.N;
-      a_rows = side.rows;
-    } else {
-      tile -= side.tiles;
-    }
-    const int nt_count = (N + BN2 - 1) / BN2;
-    k_end = Kd;
-    if (on_side) {
-      decode_tile(tile, (side.rows + BM2 - 1) / BM2, nt_count, mt, nt);
-      seg = 0;
-      row0 = mt * BM2;
-      rows = min(BM2, side.rows - row0);
-    } else if (kTN) {
+    const int tile = xcd_tile(blockIdx.x, gridDim.x, xcd_chunk);
+    if (kTN) {
       const int mt_count = (M + BM2 - 1) / BM2;
       const int per_seg = mt_count * nt_count;
       if (tile >= G * per_seg) return;
@@ -942,17 +925,11 @@ __global__ __launch_bounds__(kW4Threads, 1) void k_grouped_gemm_w4(
         }
         d[h] = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
       }
-      const u32x2 send = odd ? d[0] : d[1];
-      const uint32_t x0 = (uint32_t)__shfl_xor((int)send[0], 16, kWave);
-      const uint32_t x1 = (uint32_t)__shfl_xor((int)send[1], 16, kWave);
-      const u32x4 o = odd ? u32x4{x0, x1, d[1][0], d[1][1]} : u32x4{d[0][0], d[0][1], x0, x1};
+      const u32x4 o = pair_rows16(d[0], d[1]);
       const int c0 = n0 + cbase_e + 16 * (2 * p + (odd ? 1 : 0)) + 4 * (lg_e & ~1);
       if (c0 < N) *(u32x4*)(crow + c0) = o;
       if (EPI == kEpiGeluSave) {  // the pre-activations, paired the same way
-        const u32x2 su = odd ? us[0] : us[1];
-        const uint32_t y0 = (uint32_t)__shfl_xor((int)su[0], 16, kWave);
-        const uint32_t y1 = (uint32_t)__shfl_xor((int)su[1], 16, kWave);
-        const u32x4 ou = odd ? u32x4{y0, y1, us[1][0], us[1][1]} : u32x4{us[0][0], us[0][1], y0, y1};
+        const u32x4 ou = pair_rows16(us[0], us[1]);
         if (c0 < N) *(u32x4*)(Ep + (size_t)(row0 + m) * N + c0) = ou;
       }
     }
@@ -1063,44 +1040,8 @@ static int mt_bound_for(const GemmArgs& a, int tm) {
 template <int LAYOUT>
 constexpr bool kUseW4 = ((MOE_W4_LAYOUTS >> LAYOUT) & 1) != 0;
 
-// The two problems of a launch with a side problem, each on its own.
-static GemmArgs main_problem(const GemmArgs& a) {
-  GemmArgs m = a;
-  m.side_rows = 0;
-  return m;
-}
-static GemmArgs side_problem(const GemmArgs& a) {
-  GemmArgs s;
-  s.layout = a.layout;
-  s.epi = a.epi;
-  s.A = a.side_A;
-  s.B = a.side_B;
-  s.C = a.side_C;
-  s.E = a.side_E;
-  s.G = 1;
-  s.fixed_rows = s.max_rows = a.side_rows;
-  s.Kd = a.side_Kd;
-  s.N = a.side_N;
-  return s;
-}
-
-template <int LAYOUT, int EPI>
-static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st);
-
-// A contraction of one or two K-steps (the d_logits W_r^T accumulate: E
-// rounded up to 8) is all epilogue, which eight waves share better.
-template <int LAYOUT>
-static bool on_w4(int Kd) {
-  return kUseW4<LAYOUT> && (LAYOUT == kGemmTN || Kd > 2 * BK2);
-}
-
 template <int LAYOUT, int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
-  const bool has_side = LAYOUT != kGemmTN && a.side_rows > 0;
-  if (has_side && !(on_w4<LAYOUT>(a.Kd) && on_w4<LAYOUT>(a.side_Kd))) {
-    const hipError_t e0 = launch_bf16<LAYOUT, EPI>(main_problem(a), st);
-    return e0 != hipSuccess ? e0 : launch_bf16<LAYOUT, EPI>(side_problem(a), st);
-  }
   const hipError_t e = allow_dynamic_lds<k_grouped_gemm_bf16<LAYOUT, EPI>, true>();
   if (e != hipSuccess) return e;
   const int ntc = (a.N + BN2 - 1) / BN2;
@@ -1112,20 +1053,16 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
     mtb = mt_bound_for(a, BM2);
     grid = (long long)mtb * ntc;
   }
-  GemmSide side{(const bf16*)a.side_A, (const bf16*)a.side_B, a.side_C, (bf16*)a.side_E,
-                a.side_rows, a.side_Kd, a.side_N, 0};
-  if (has_side) {
-    side.tiles = ((a.side_rows + BM2 - 1) / BM2) * ((a.side_N + BN2 - 1) / BN2);
-    grid += side.tiles;
-  }
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (on_w4<LAYOUT>(a.Kd)) {
+  // A contraction of one or two K-steps (the d_logits W_r^T accumulate: E
+  // rounded up to 8) is all epilogue, which eight waves share better.
+  if (kUseW4<LAYOUT> && (LAYOUT == kGemmTN || a.Kd > 2 * BK2)) {
     const hipError_t e4 = allow_dynamic_lds<k_grouped_gemm_w4<LAYOUT, EPI>, true>();
     if (e4 != hipSuccess) return e4;
     k_grouped_gemm_w4<LAYOUT, EPI><<<(unsigned)grid, kW4Threads, kSmem2, st>>>(
         (const bf16*)a.A, (const bf16*)a.B, a.C, (bf16*)a.E, a.offsets, a.G, a.fixed_rows,
-        a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N, xcd_chunk_for(ntc), side);
+        a.offsets ? a.max_rows : a.fixed_rows, mtb, a.M, a.Kd, a.N, xcd_chunk_for(ntc));
     return hipGetLastError();
   }
   k_grouped_gemm_bf16<LAYOUT, EPI><<<(unsigned)grid, kGemmThreads, kSmem2, st>>>(
@@ -1136,10 +1073,6 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t st) {
 
 template <int LAYOUT, int EPI>
 static hipError_t launch_f32(const GemmArgs& a, hipStream_t st) {
-  if (LAYOUT != kGemmTN && a.side_rows > 0) {
-    const hipError_t e0 = launch_f32<LAYOUT, EPI>(main_problem(a), st);
-    return e0 != hipSuccess ? e0 : launch_f32<LAYOUT, EPI>(side_problem(a), st);
-  }
   const int ntc = (a.N + 63) / 64;
   int mtb = 0;
   long long grid;

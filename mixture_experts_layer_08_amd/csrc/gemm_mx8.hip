@@ -617,15 +617,25 @@ __global__ __launch_bounds__(kMxW4Threads, 1) void k_grouped_gemm_mx8w4(
         v[r] = EPI == kMxEpiGeluQuantOperand ? gelu_tanh_f32(acc[i][j][r]) : acc[i][j][r];
         amax = fmaxf(amax, fabsf(v[r]));
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      // The exchanges between lanes l and l ^ 32 use v_permlane32_swap, which
+      // trades the upper half-wave of its first operand for the lower
+      // half-wave of its second, in the VALU: swapping a value with itself
+      // leaves each lane its own value and its partner's, in some order.
+      {
+        const auto am = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax),
+                                                         __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(am[0]), __uint_as_float(am[1]));
+      }
       const uint32_t code = mx_scale_code(amax);
       const float inv = mx_inv_scale(code);
       uint32_t d[4];  // columns 8g + 4kh .. +3 of the block
 #pragma unroll
       for (int g = 0; g < 4; ++g) d[g] = mx_encode4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], inv);
-      const uint32_t x0 = __shfl_xor(kh ? d[0] : d[2], 32, kWave);
-      const uint32_t x1 = __shfl_xor(kh ? d[1] : d[3], 32, kWave);
-      const u32x4 o = kh ? u32x4{x0, d[2], x1, d[3]} : u32x4{d[0], x0, d[1], x1};
+      // lower half: its own d[0] and its partner's, its own d[1] and its
+      // partner's; upper half: its partner's d[2] and its own, likewise d[3]
+      const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+      const u32x4 o = u32x4{s0[0], s0[1], s1[0], s1[1]};
       if (m < rows && nb < N) {
         *(u32x4*)(C + (size_t)(row0 + m) * N + nb + 16 * kh) = o;
         if (kh == 0) {

@@ -118,18 +118,6 @@ struct GemmArgs {
   int M = 0;                       // TN: rows of each C block (columns of A)
   int Kd = 0;                      // NN / NT: contraction length
   int N = 0;                       // columns of B and C
-  // Optional second problem of the row-major forms, run in the same launch
-  // where the kernel allows (else as a launch of its own after the first):
-  // C2 = act(A2 [side_rows][side_Kd] * B2 [side_Kd][side_N]), one fixed
-  // segment, same layout and epilogue (side_E its epilogue tensor).  The
-  // forward's shared expert.  side_rows = 0: none.
-  const void* side_A = nullptr;
-  const void* side_B = nullptr;
-  void* side_C = nullptr;
-  void* side_E = nullptr;
-  int side_rows = 0;
-  int side_Kd = 0;
-  int side_N = 0;
 };
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& a, hipStream_t st);

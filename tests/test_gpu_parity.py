@@ -266,13 +266,11 @@ EDGE = [
     # a shared expert as wide as the routed ones (T = 700 leaves its launch a
     # 188-row last tile)
     ("shared_as_wide", dict(T=700, H=128, E=16, K=4, h=96, hs=96, cf=1.25, bias="normal")),
-    # the shared expert's tiles share the routed launches' grid when both
-    # contractions exceed two K-steps: here 3 x 2 shared tiles in GEMM1 and
-    # 3 x 2 in GEMM2 beside ragged routed segments, widths unlike the routed
-    # ones; and one whose GEMM2 contraction (hs = 64) runs as its own launch
-    ("shared_in_routed_grid", dict(T=700, H=320, E=8, K=2, h=200, hs=392, cf=1.25,
-                                   bias="normal")),
-    ("shared_own_launch", dict(T=600, H=192, E=8, K=2, h=136, hs=64, cf=1.25)),
+    # a shared expert of 3 x 2 tiles in both of its GEMMs, wider than the
+    # routed experts; and one whose GEMM2 contraction (hs = 64, two K-steps)
+    # runs on the eight-wave kernel
+    ("shared_multi_tile", dict(T=700, H=320, E=8, K=2, h=200, hs=392, cf=1.25, bias="normal")),
+    ("shared_short_k", dict(T=600, H=192, E=8, K=2, h=136, hs=64, cf=1.25)),
     ("E40_E_not_pow2", dict(T=700, H=256, E=40, K=3, h=264, cf=1.0, bias="normal")),
     ("E128_hot", dict(T=640, H=128, E=128, K=2, h=96, cf=0.0, bias="hot01")),
     # the bf16 router stages its weights in chunks of KC = 512 / 128 / 32 k
